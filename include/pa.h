@@ -1,0 +1,190 @@
+/*
+ * pa.h — C ABI of libpa: paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the pages this library is built from:
+ *   - "Module 4 · Batching, Scheduling, and Paging" (datasystem.school),
+ *     section "PagedAttention": each sequence's KV cache is split into
+ *     fixed-size blocks stored non-contiguously, with a per-sequence block
+ *     table mapping logical blocks to physical ones; attention gathers K and V
+ *     through that indirection. Section "Block sharing": a shared prefix block
+ *     is copied on the first divergent write.
+ *   - "Paging the KV Cache" (lecture 6), section "The waste hiding inside
+ *     memory": the cache grows token by token.
+ *   - worksonmygpu.com continuous-batching post, section "Selective batching":
+ *     each request's query attends only over that request's own tokens with
+ *     softmax(Q K^T / sqrt(d_k)) V; section "The prefill/decode mix": prefill
+ *     chunks run in the same iteration as decode steps.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every call
+ * ---------------------------------------------------------------------------
+ * Pointers. Every buffer pointer is a device pointer (HIP device memory) owned
+ * by the caller; pool, query, K/V-row and output pointers must be 16-byte
+ * aligned (kernels move 16-byte vectors). libpa allocates nothing, frees nothing and keeps no global
+ * state; calls on different streams with disjoint buffers are independent.
+ *
+ * Streams. `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ * Every call only enqueues work on `stream` and returns: no host
+ * synchronisation, no device-to-host read. Calls that depend on each other
+ * must be issued in order on one stream: copy_blocks, then append_kv, then
+ * decode / prefill_chunk.
+ *
+ * Element type. `dtype` is PA_F32 (float) or PA_BF16 (bfloat16). Queries,
+ * pool, new K/V rows and outputs share it. Scores, softmax and accumulation
+ * are float32; bfloat16 outputs are rounded to nearest even.
+ *
+ * KV pool layout (one layer). The pool is `num_blocks` blocks of
+ * `2 * num_kv_heads * block_size * head_dim` elements each. Block j holds
+ *   K half: [num_kv_heads][block_size][head_dim]  (a token's vector contiguous)
+ *   V half: [num_kv_heads][head_dim][block_size]  (a dimension's block_size
+ *                                                  token values contiguous)
+ * K element (block j, kv head g, slot s, dim i) is at
+ *   j*E + (g*block_size + s)*head_dim + i,                     E = 2*Hkv*bs*d;
+ * V element (j, g, s, i) is at
+ *   j*E + Hkv*bs*d + (g*head_dim + i)*block_size + s.
+ * Logical token t of a sequence with table row T lives in block T[t / bs] at
+ * slot t % bs. A slot number is `block * block_size + offset`.
+ *
+ * Supported shapes: head_dim in {64, 128}; block_size in {16, 32};
+ * num_q_heads = G * num_kv_heads with G in {1, 2, 4, 8}; query head h reads
+ * kv head h / G.
+ *
+ * Errors. Arguments are validated on the host before anything is enqueued;
+ * a non-zero return means nothing was enqueued. Device-side *contents* are
+ * the caller's contract: block ids and slots must lie in [0, num_blocks) and
+ * [0, num_blocks*block_size); context lengths in [0, max_blocks_per_seq *
+ * block_size]. Kernels clamp out-of-range block ids and lengths so that they
+ * never access memory outside the buffers, but the result is then unspecified.
+ * A launch failure returns PA_ERR_LAUNCH.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* inconsistent or negative sizes */
+  PA_ERR_UNSUPPORTED = 3, /* head_dim / block_size / group size / dtype not built */
+  PA_ERR_WORKSPACE = 4,   /* workspace too small */
+  PA_ERR_LAUNCH = 5,      /* the HIP launch failed */
+  PA_ERR_ALIAS = 6,       /* output overlaps an input it must not overlap */
+  PA_ERR_ALIGN = 7        /* a data pointer is not 16-byte aligned */
+};
+
+/* Tokens per split-K partition of pa_decode. A sequence of n tokens is cut at
+ * multiples of PA_DECODE_PARTITION; the cut never depends on the rest of the
+ * batch, so a sequence's output does not depend on batch composition. */
+#define PA_DECODE_PARTITION 512
+
+/*
+ * pa_append_kv — write each new token's K and V into its block slot.
+ * ("Paging the KV Cache", "The waste hiding inside memory": the cache grows
+ * one token at a time; "Module 4", "PagedAttention": the slot's block comes
+ * from the sequence's table.)
+ *
+ *   kv_pool      [num_blocks * E] pool, modified in place
+ *   k_new, v_new [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping [num_tokens] int32: token i goes to slot slot_mapping[i];
+ *                a negative slot skips the token (padding).
+ * Copies are bitwise. Two tokens with the same slot in one call: undefined.
+ * num_tokens == 0 is a valid no-op.
+ */
+int pa_append_kv(void* kv_pool, const void* k_new, const void* v_new,
+                 const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                 int32_t dtype, void* stream);
+
+/*
+ * pa_copy_blocks — copy-on-write of whole blocks.
+ * ("Module 4", section "Block sharing": on the first divergent write to a
+ * shared block, the block is copied.)
+ *
+ *   block_pairs [num_pairs][2] int32 (src, dst): block dst becomes a bitwise
+ *               copy of block src (K and V halves, all heads, all slots).
+ * Every dst must be distinct and no dst may be the src of another pair
+ * (otherwise undefined). num_pairs == 0 is a valid no-op.
+ */
+int pa_copy_blocks(void* kv_pool, const int32_t* block_pairs, int32_t num_pairs,
+                   int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int32_t dtype, void* stream);
+
+/*
+ * pa_decode_workspace_size — bytes of workspace pa_decode needs for a batch of
+ * `num_seqs` sequences whose longest context is at most `max_context_len`.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_context_len);
+
+/*
+ * pa_decode — one decode step of paged attention for a ragged batch.
+ * (worksonmygpu.com continuous-batching post, "Selective batching": per
+ * request softmax(q K^T * scale) V over that request's own tokens; "Module 4",
+ * "PagedAttention": K and V gathered through the block table.)
+ *
+ *   out           [num_seqs][num_q_heads][head_dim]  (must not overlap q)
+ *   q             [num_seqs][num_q_heads][head_dim]
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32 physical block ids;
+ *                 entries at or past ceil(n/bs) are never read.
+ *   context_lens  [num_seqs] int32: sequence b attends to its logical tokens
+ *                 0 .. context_lens[b]-1 (including a token appended this
+ *                 step). A zero length gives a zero output row. Slots past
+ *                 the context are never used, even when they hold NaN.
+ *   max_context_len  host-side upper bound of context_lens (sizes the grid).
+ *   scale         multiplies q.K (1/sqrt(head_dim) for standard attention).
+ *   workspace     device buffer of at least pa_decode_workspace_size() bytes,
+ *                 ZERO-FILLED before its first use. Each call leaves it ready
+ *                 for the next call (its counters return to zero), so it can
+ *                 be reused across calls and layers; calls that may run
+ *                 concurrently need separate workspaces.
+ */
+int pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+              const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+              int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+              int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+              int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill_chunk — attention of prefill chunks over a paged cache.
+ * (worksonmygpu.com continuous-batching post, "The prefill/decode mix":
+ * prompt chunks share the iteration with decode steps.)
+ *
+ * Chunk c's queries are rows query_start_loc[c] .. query_start_loc[c+1]-1 of
+ * q; they are the last L_c of the chunk's context_lens[c] tokens, whose K/V
+ * must already be appended. Query i of the chunk sits at position
+ * a = context_lens[c] - L_c + i and attends to tokens 0..a (causal within the
+ * chunk, full over earlier cached tokens).
+ *
+ *   out            [total_q_tokens][num_q_heads][head_dim]  (must not overlap q)
+ *   q              [total_q_tokens][num_q_heads][head_dim]
+ *   block_tables   [num_chunks][max_blocks_per_seq] int32
+ *   context_lens   [num_chunks] int32, each >= its chunk length
+ *   query_start_loc [num_chunks + 1] int32 device array, non-decreasing,
+ *                  query_start_loc[0] = 0, query_start_loc[num_chunks] =
+ *                  total_q_tokens
+ *   max_chunk_len  host-side upper bound of the chunk lengths (sizes the grid)
+ */
+int pa_prefill_chunk(void* out, const void* q, const void* kv_pool,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* query_start_loc, int32_t num_chunks,
+                     int32_t total_q_tokens, int32_t max_chunk_len,
+                     int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                     int32_t dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,190 @@
+"""Python binding of libpa: paged KV-cache attention for AMD Instinct MI355X (gfx950).
+
+Argument marshalling only. Every function forwards raw device pointers, sizes
+and torch's current HIP stream to the C ABI declared in include/pa.h and raises
+``PAError`` on a non-zero status; all work runs in libpa's HIP kernels. There
+is no fallback: if libpa.so is not built the first call raises.
+
+Tensors must be contiguous CUDA (HIP) tensors; index tensors are int32; the
+pool is any contiguous tensor of ``num_blocks * 2 * Hkv * block_size *
+head_dim`` elements of the attention dtype (float32 or bfloat16).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["PAError", "load", "lib_path", "pa_append_kv", "pa_copy_blocks", "pa_decode",
+           "pa_decode_workspace_size", "pa_prefill_chunk", "pa_status_string",
+           "new_decode_workspace", "DECODE_PARTITION"]
+
+DECODE_PARTITION = 512  # PA_DECODE_PARTITION in include/pa.h
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libpa.so"
+_lib = None
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+_c_int = ctypes.c_int32
+_c_ptr = ctypes.c_void_p
+
+
+class PAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {pa_status_string(status)}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load() -> ctypes.CDLL:
+    """Load libpa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m paged_kv_cache_282_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.pa_append_kv.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int,
+                                 _c_int, _c_int, _c_ptr]
+    lib.pa_append_kv.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   _c_ptr]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_decode_workspace_size.argtypes = [_c_int, _c_int, _c_int, _c_int]
+    lib.pa_decode_workspace_size.restype = ctypes.c_size_t
+    lib.pa_decode.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int,
+                              _c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _c_int,
+                              _c_ptr, ctypes.c_size_t, _c_ptr]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_prefill_chunk.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int,
+                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     _c_int, ctypes.c_float, _c_int, _c_ptr]
+    lib.pa_prefill_chunk.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def pa_status_string(status: int) -> str:
+    return load().pa_status_string(int(status)).decode()
+
+
+# -- marshalling helpers ---------------------------------------------------------
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _i32(t: torch.Tensor, name: str) -> int:
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return _dev(t, name)
+
+
+def _dtype_code(*ts: torch.Tensor) -> int:
+    dt = ts[0].dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}; use float32 or bfloat16")
+    for t in ts[1:]:
+        if t.dtype != dt:
+            raise TypeError("query, pool, K/V rows and output must share one dtype")
+    return _DTYPES[dt]
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _num_blocks(pool: torch.Tensor, hkv: int, bs: int, d: int) -> int:
+    per = 2 * hkv * bs * d
+    if pool.numel() % per:
+        raise ValueError(f"pool has {pool.numel()} elements, not a multiple of the block size {per}")
+    return pool.numel() // per
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PAError(fn, status)
+
+
+# -- the C ABI, one function each ------------------------------------------------
+
+def pa_append_kv(kv_pool, k_new, v_new, slot_mapping, block_size: int, stream=None) -> None:
+    """Write k_new/v_new [T][Hkv][d] into the pool slots ``slot_mapping`` [T] (int32)."""
+    T, hkv, d = k_new.shape
+    nb = _num_blocks(kv_pool, hkv, block_size, d)
+    _check("pa_append_kv", load().pa_append_kv(
+        _dev(kv_pool, "kv_pool"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _i32(slot_mapping, "slot_mapping"), T, nb, hkv, d, block_size,
+        _dtype_code(kv_pool, k_new, v_new), _stream(stream)))
+
+
+def pa_copy_blocks(kv_pool, block_pairs, num_kv_heads: int, head_dim: int, block_size: int,
+                   stream=None) -> None:
+    """Copy whole blocks: ``block_pairs`` [P][2] int32 of (src, dst)."""
+    nb = _num_blocks(kv_pool, num_kv_heads, block_size, head_dim)
+    P = block_pairs.shape[0] if block_pairs.numel() else 0
+    _check("pa_copy_blocks", load().pa_copy_blocks(
+        _dev(kv_pool, "kv_pool"), _i32(block_pairs, "block_pairs") if P else None, P, nb,
+        num_kv_heads, head_dim, block_size, _dtype_code(kv_pool), _stream(stream)))
+
+
+def pa_decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int,
+                             max_context_len: int) -> int:
+    return int(load().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len))
+
+
+def new_decode_workspace(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
+                         device="cuda") -> torch.Tensor:
+    """A zero-filled workspace of the size pa_decode needs."""
+    n = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len: int,
+              num_kv_heads: int, block_size: int, scale: float, workspace, stream=None):
+    """Paged decode attention; fills ``out`` [B][Hq][d] and returns it."""
+    B, hq, d = q.shape
+    nb = _num_blocks(kv_pool, num_kv_heads, block_size, d)
+    mb = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    _check("pa_decode", load().pa_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(kv_pool, "kv_pool"),
+        _i32(block_tables, "block_tables"), _i32(context_lens, "context_lens"), B, mb,
+        int(max_context_len), hq, num_kv_heads, d, block_size, nb, float(scale),
+        _dtype_code(q, kv_pool, out), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def pa_prefill_chunk(out, q, kv_pool, block_tables, context_lens, query_start_loc,
+                     max_chunk_len: int, num_kv_heads: int, block_size: int, scale: float,
+                     stream=None):
+    """Chunked-prefill attention; fills ``out`` [sum L][Hq][d] and returns it."""
+    T, hq, d = q.shape
+    C = context_lens.shape[0]
+    nb = _num_blocks(kv_pool, num_kv_heads, block_size, d)
+    mb = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    _check("pa_prefill_chunk", load().pa_prefill_chunk(
+        _dev(out, "out"), _dev(q, "q"), _dev(kv_pool, "kv_pool"),
+        _i32(block_tables, "block_tables"), _i32(context_lens, "context_lens"),
+        _i32(query_start_loc, "query_start_loc"), C, T, int(max_chunk_len), mb, hq,
+        num_kv_heads, d, block_size, nb, float(scale), _dtype_code(q, kv_pool, out),
+        _stream(stream)))
+    return out

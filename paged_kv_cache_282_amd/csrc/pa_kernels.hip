@@ -1,0 +1,915 @@
+// Device code of libpa: KV append, block copy, paged decode and chunked-prefill
+// attention for CDNA4 (gfx950, wave64).
+//
+// What is computed follows the pages:
+//   * "Module 4 · Batching, Scheduling, and Paging", section "PagedAttention":
+//     K/V live in fixed-size blocks reached through a per-sequence block table;
+//     the kernels gather through that indirection. Section "Block sharing":
+//     shared blocks are copied on the first divergent write.
+//   * worksonmygpu.com continuous-batching post, section "Selective batching":
+//     each request attends over its own tokens, softmax(q K^T * scale) V;
+//     section "The prefill/decode mix": prefill chunks in the same iteration.
+//
+// How it is computed is this file's own design for gfx950:
+//   * One workgroup (4 waves) per (sequence, kv head, 512-token partition).
+//     Waves take interleaved 32-token steps of the partition, keep an online
+//     softmax state each, merge in LDS, and the last-arriving workgroup of a
+//     sequence merges the partitions (log-sum-exp identity) and writes out.
+//   * bf16: scores and p.V run on v_mfma_f32_16x16x32_bf16. The 16 columns of
+//     each MFMA are the query heads of one GQA group (padded) or, in prefill,
+//     (position, head) rows. K tokens are assigned to MFMA rows so that each
+//     lane's eight scores are exactly the eight tokens whose V^T values the
+//     same lane loads as one 16-byte operand for p.V: probabilities never
+//     leave registers. V is stored dimension-major in the pool for this.
+//   * Tokens outside a context are excluded by selection (-inf scores, zeroed
+//     V), never by multiplying with p = 0, so NaN in unused slots is harmless.
+//   * fp32: a VALU kernel with the same work decomposition (16 lanes per token
+//     for q.K, dimension-owning lanes for p.V).
+#include "pa_launch.h"
+
+#include <stdint.h>
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_over_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+// Sum over the 16 lanes of a group; every lane receives the total.
+__device__ __forceinline__ float sum_over_row16(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  return x + __shfl_xor(x, 8);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(T* p, float v);
+template <>
+__device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
+  *p = f32_to_bf16_bits(v);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of the chip. Giving
+// each XCD a contiguous range of logical items keeps the partitions of one
+// (sequence, kv head) -- and the merge that reads them -- on one L2.
+__device__ __forceinline__ int xcd_remap(int wid, int nwg) {
+  const int per = nwg >> 3;  // nwg is a multiple of 8
+  return (wid & 7) * per + (wid >> 3);
+}
+
+__device__ __forceinline__ int clamp_block(int blk, int64_t nb) {
+  return (static_cast<uint32_t>(blk) < static_cast<uint64_t>(nb)) ? blk : 0;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA engine: online-softmax attention of NT column tiles of 16 query
+// rows over 32-token steps of one kv head.
+//
+// Lane (kg = lane/16, r = lane%16):
+//   score MFMA  S^T[tok][row] = K[tok][:] . Q[row][:]
+//     A (K)  lane gives K[T(r)][32s + 8kg .. +7]   (set a: T = 8(r/4) + r%4,
+//                                                  set b: T + 4)
+//     B (Q)  lane gives Q[row r][32s + 8kg .. +7]
+//     C      lane (kg, n) gets tokens 8kg+i (set a) and 8kg+4+i (set b), i<4,
+//            of row n: the eight tokens 8kg .. 8kg+7.
+//   p.V MFMA   O^T[dim][row] += V^T[dim][tok] . P^T[tok][row]
+//     A (V^T) lane gives V^T[16j + r][tok 8kg .. +7]  (16 contiguous bytes)
+//     B (P)   lane gives P[row n][tok 8kg .. +7]      (its own eight scores)
+//     C       lane (kg, n) holds O^T[16j + 4kg + i][n], i < 4.
+// ---------------------------------------------------------------------------
+template <int D, int BS, int NT>
+struct Bf16Engine {
+  static constexpr int KS = D / 32;
+  static constexpr int VT = D / 16;
+  bf16x8 qreg[NT][KS];
+  f32x4 o[NT][VT];
+  float m[NT], l[NT];
+  int lim[NT];  // last token this lane's row may attend to (-1: none)
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      m[nt] = -__builtin_inff();
+      l[nt] = 0.f;
+      lim[nt] = -1;
+#pragma unroll
+      for (int j = 0; j < VT; ++j) o[nt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qreg[nt][s] = bf16x8{};
+    }
+  }
+
+  // Load row `nt`'s query (lane's 8-element slices) from q_row (nullptr: zero).
+  __device__ __forceinline__ void load_q(int nt, const uint16_t* q_row, int kg) {
+    if (q_row == nullptr) return;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qreg[nt][s] = __builtin_bit_cast(bf16x8, ld16(q_row + 32 * s + 8 * kg));
+  }
+
+  // One 32-token step starting at logical token t0. Tokens t0..t0+15 live in
+  // block blkA and t0+16..t0+31 in blkB (bs 16) or all in blkA (bs 32).
+  // Tokens >= vend have their V zeroed (they may be NaN); scores of tokens past
+  // a row's limit are -inf.
+  __device__ __forceinline__ void step(const uint16_t* __restrict__ pool, int64_t blk_elems,
+                                       int64_t kofs, int64_t vofs, int blkA, int blkB, int t0,
+                                       int vend, int lane, float sl2e) {
+    const int r = lane & 15, kg = lane >> 4;
+    const uint16_t* baseA = pool + static_cast<int64_t>(blkA) * blk_elems;
+    const uint16_t* baseB = pool + static_cast<int64_t>(blkB) * blk_elems;
+    const int ta = ((r >> 2) << 3) | (r & 3);
+    const int tb = ta + 4;
+    const uint16_t* ka;
+    const uint16_t* kb;
+    if constexpr (BS == 16) {
+      ka = (ta < 16 ? baseA : baseB) + kofs + (ta & 15) * D + 8 * kg;
+      kb = (tb < 16 ? baseA : baseB) + kofs + (tb & 15) * D + 8 * kg;
+    } else {
+      ka = baseA + kofs + ta * D + 8 * kg;
+      kb = baseA + kofs + tb * D + 8 * kg;
+    }
+    const uint16_t* vp;
+    if constexpr (BS == 16)
+      vp = (kg < 2 ? baseA : baseB) + vofs + 8 * (kg & 1);
+    else
+      vp = baseA + vofs + 8 * kg;
+
+    u32x4 kA[KS], kB[KS], vv[VT];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kA[s] = ld16(ka + 32 * s);
+      kB[s] = ld16(kb + 32 * s);
+    }
+#pragma unroll
+    for (int j = 0; j < VT; ++j) vv[j] = ld16(vp + (16 * j + r) * BS);
+
+    if (t0 + 32 > vend) {  // wave-uniform: zero V of tokens past the end
+      const int nvalid = vend - t0 - 8 * kg;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t mask = (2 * w < nvalid ? 0x0000FFFFu : 0u) |
+                              (2 * w + 1 < nvalid ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int j = 0; j < VT; ++j) vv[j][w] &= mask;
+      }
+    }
+
+    const int tbase = t0 + 8 * kg;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kA[s]),
+                                                     qreg[nt][s], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kB[s]),
+                                                     qreg[nt][s], sb, 0, 0, 0);
+      }
+      float sc[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[i] = sa[i] * sl2e;
+        sc[4 + i] = sb[i] * sl2e;
+      }
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sc[e] = (tbase + e <= lim[nt]) ? sc[e] : -__builtin_inff();
+        mx = fmaxf(mx, sc[e]);
+      }
+      mx = max_over_groups(mx);
+      const float mnew = fmaxf(m[nt], mx);
+      const float muse = (mnew == -__builtin_inff()) ? 0.f : mnew;
+      const float alpha = exp2_fast(m[nt] - muse);
+      bf16x8 p;
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 pb = static_cast<__bf16>(exp2_fast(sc[e] - muse));
+        p[e] = pb;
+        ps += static_cast<float>(pb);
+      }
+      l[nt] = l[nt] * alpha + ps;
+      m[nt] = mnew;
+#pragma unroll
+      for (int j = 0; j < VT; ++j) {
+        o[nt][j] *= alpha;
+        o[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv[j]), p,
+                                                           o[nt][j], 0, 0, 0);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// fp32 VALU engine: G query rows (one GQA group) of one kv head.
+// Lane (grp = lane/16, c = lane%16). In a 32-token step, group grp owns tokens
+// 8grp .. 8grp+7. q.K: lane holds dims c*EPL .. +EPL of a K row; the 16 lanes
+// sum their partial dot products. p.V: lane owns dims c + 16k and reads 8
+// consecutive tokens of each from the dimension-major V half.
+// ---------------------------------------------------------------------------
+template <int D, int BS, int G>
+struct F32Engine {
+  static constexpr int EPL = D / 16;
+  float qv[G][EPL];
+  float acc[G][EPL];
+  float m[G], l[G];
+  int lim;  // last token the rows may attend to (uniform)
+
+  __device__ __forceinline__ void init(const float* q_rows, int c) {
+    // q_rows: G consecutive rows of D floats (nullptr: no rows)
+#pragma unroll
+    for (int qi = 0; qi < G; ++qi) {
+      m[qi] = -__builtin_inff();
+      l[qi] = 0.f;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) {
+        acc[qi][k] = 0.f;
+        qv[qi][k] = q_rows ? q_rows[qi * D + c * EPL + k] : 0.f;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void step(const float* __restrict__ pool, int64_t blk_elems,
+                                       int64_t kofs, int64_t vofs, int blkA, int blkB, int t0,
+                                       int vend, int lane, float sl2e) {
+    const int grp = lane >> 4, c = lane & 15;
+    const float* base;
+    int slot0;
+    if constexpr (BS == 16) {
+      base = pool + static_cast<int64_t>(grp < 2 ? blkA : blkB) * blk_elems;
+      slot0 = 8 * (grp & 1);
+    } else {
+      base = pool + static_cast<int64_t>(blkA) * blk_elems;
+      slot0 = 8 * grp;
+    }
+    const int tbase = t0 + 8 * grp;
+    float s[8][G];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float* kr = base + kofs + (slot0 + e) * D + c * EPL;
+      float kv[EPL];
+#pragma unroll
+      for (int k4 = 0; k4 < EPL / 4; ++k4) {
+        const u32x4 w = ld16(kr + 4 * k4);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) kv[4 * k4 + x] = __builtin_bit_cast(float, w[x]);
+      }
+      const bool valid = tbase + e <= lim;
+#pragma unroll
+      for (int qi = 0; qi < G; ++qi) {
+        float part = 0.f;
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) part = fmaf(kv[k], qv[qi][k], part);
+        part = sum_over_row16(part);
+        s[e][qi] = valid ? part * sl2e : -__builtin_inff();
+      }
+    }
+#pragma unroll
+    for (int qi = 0; qi < G; ++qi) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[e][qi]);
+      mx = max_over_groups(mx);
+      const float mnew = fmaxf(m[qi], mx);
+      const float muse = (mnew == -__builtin_inff()) ? 0.f : mnew;
+      const float alpha = exp2_fast(m[qi] - muse);
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s[e][qi] = exp2_fast(s[e][qi] - muse);
+        ps += s[e][qi];
+      }
+      l[qi] = l[qi] * alpha + ps;
+      m[qi] = mnew;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) acc[qi][k] *= alpha;
+    }
+    const bool tail = t0 + 32 > vend;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+      const float* vr = base + vofs + (c + 16 * k) * BS + slot0;
+      float v[8];
+      const u32x4 w0 = ld16(vr), w1 = ld16(vr + 4);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        v[x] = __builtin_bit_cast(float, w0[x]);
+        v[4 + x] = __builtin_bit_cast(float, w1[x]);
+      }
+      if (tail) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (tbase + e < vend) ? v[e] : 0.f;
+      }
+#pragma unroll
+      for (int qi = 0; qi < G; ++qi)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[qi][k] = fmaf(s[e][qi], v[e], acc[qi][k]);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Workgroup-level merge of the per-wave states held in LDS.
+// ---------------------------------------------------------------------------
+template <int D>
+struct MergeSmem {
+  float o[kWaves][16][D];
+  float m[kWaves][16];
+  float l[kWaves][16];
+  int last;
+};
+
+// Combines the kWaves states of row `row` at dimension `dd`: (M, L, O).
+template <int D>
+__device__ __forceinline__ void combine_waves(const MergeSmem<D>& sm, int row, int dd, float& M,
+                                              float& L, float& O) {
+  M = -__builtin_inff();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][row]);
+  L = 0.f;
+  O = 0.f;
+  if (M == -__builtin_inff()) return;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float f = exp2_fast(sm.m[w][row] - M);
+    L = fmaf(sm.l[w][row], f, L);
+    O = fmaf(sm.o[w][row][dd], f, O);
+  }
+}
+
+// After each wave has written its state, either store the normalised output
+// (single partition) or publish this partition's state and let the last
+// partition to finish merge all of them.
+template <int D, typename OutT>
+__device__ __forceinline__ void finish_partition(MergeSmem<D>& sm, int rows, int np, int p,
+                                                 int np_max, OutT* __restrict__ out_rows,
+                                                 float* __restrict__ ws_o,
+                                                 float* __restrict__ ws_ml,
+                                                 int32_t* __restrict__ counter) {
+  // out_rows: rows * D outputs; ws_o / ws_ml: this (sequence, group)'s first
+  // row's partials, rows spaced np_max * D (resp. np_max * 2) apart.
+  if (np == 1) {
+    for (int idx = threadIdx.x; idx < rows * D; idx += kWaves * 64) {
+      const int row = idx / D, dd = idx - row * D;
+      float M, L, O;
+      combine_waves<D>(sm, row, dd, M, L, O);
+      store_out<OutT>(out_rows + idx, L > 0.f ? O / L : 0.f);
+    }
+    return;
+  }
+  for (int idx = threadIdx.x; idx < rows * D; idx += kWaves * 64) {
+    const int row = idx / D, dd = idx - row * D;
+    float M, L, O;
+    combine_waves<D>(sm, row, dd, M, L, O);
+    ws_o[(static_cast<int64_t>(row) * np_max + p) * D + dd] = O;
+    if (dd == 0) {
+      ws_ml[(static_cast<int64_t>(row) * np_max + p) * 2 + 0] = M;
+      ws_ml[(static_cast<int64_t>(row) * np_max + p) * 2 + 1] = L;
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = atomicAdd(counter, 1);
+    sm.last = (prev == np - 1);
+    if (prev == np - 1) atomicExch(counter, 0);  // ready for the next call
+  }
+  __syncthreads();
+  if (!sm.last) return;
+  __threadfence();
+  for (int idx = threadIdx.x; idx < rows * D; idx += kWaves * 64) {
+    const int row = idx / D, dd = idx - row * D;
+    const float* mlr = ws_ml + static_cast<int64_t>(row) * np_max * 2;
+    const float* orow = ws_o + static_cast<int64_t>(row) * np_max * D + dd;
+    float M = -__builtin_inff();
+    for (int pp = 0; pp < np; ++pp) M = fmaxf(M, mlr[2 * pp]);
+    float L = 0.f, O = 0.f;
+    if (M != -__builtin_inff()) {
+      for (int pp = 0; pp < np; ++pp) {
+        const float f = exp2_fast(mlr[2 * pp] - M);
+        L = fmaf(mlr[2 * pp + 1], f, L);
+        O = fmaf(orow[static_cast<int64_t>(pp) * D], f, O);
+      }
+    }
+    store_out<OutT>(out_rows + idx, L > 0.f ? O / L : 0.f);
+  }
+}
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* pool;
+  const int32_t* tables;
+  const int32_t* lens;
+  int num_seqs, mb, hq, hkv, max_ctx, np_max, n_items;
+  int64_t nb, blk_elems;
+  float sl2e;
+  float* ws_o;
+  float* ws_ml;
+  int32_t* ws_cnt;
+};
+
+// Resolves (sequence, kv head, partition) of this workgroup; false if idle.
+struct DecodeItem {
+  int b, g, p, np, tok0, tok1;
+};
+template <int BS>
+__device__ __forceinline__ bool decode_item(const DecodeArgs& a, DecodeItem& it) {
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  if (item >= a.n_items) return false;
+  const int bg = item / a.np_max;
+  it.p = item - bg * a.np_max;
+  it.b = bg / a.hkv;
+  it.g = bg - it.b * a.hkv;
+  int n = a.lens[it.b];
+  n = n < 0 ? 0 : n;
+  n = n > a.max_ctx ? a.max_ctx : n;
+  n = n > a.mb * BS ? a.mb * BS : n;
+  it.np = n > 0 ? (n + kPartition - 1) / kPartition : 1;
+  if (it.p >= it.np) return false;
+  it.tok0 = it.p * kPartition;
+  it.tok1 = min(n, it.tok0 + kPartition);
+  return true;
+}
+
+template <int BS>
+__device__ __forceinline__ void step_blocks(const int32_t* __restrict__ trow, int t0, int vend,
+                                            int64_t nb, int& blkA, int& blkB) {
+  if constexpr (BS == 16) {
+    blkA = trow[t0 >> 4];
+    blkB = (t0 + 16 < vend) ? trow[(t0 >> 4) + 1] : blkA;
+  } else {
+    blkA = trow[t0 >> 5];
+    blkB = blkA;
+  }
+  blkA = clamp_block(blkA, nb);
+  blkB = clamp_block(blkB, nb);
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
+  DecodeItem it;
+  if (!decode_item<BS>(a, it)) return;
+  __shared__ MergeSmem<D> sm;
+  const int G = a.hq / a.hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, kg = lane >> 4;
+  const uint16_t* pool = static_cast<const uint16_t*>(a.pool);
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+
+  Bf16Engine<D, BS, 1> eng;
+  eng.init();
+  if (r < G) {
+    eng.load_q(0, q + (static_cast<int64_t>(it.b) * a.hq + it.g * G + r) * D, kg);
+    eng.lim[0] = it.tok1 - 1;
+  }
+  const int64_t kofs = static_cast<int64_t>(it.g) * BS * D;
+  const int64_t vofs = static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(it.g) * D * BS;
+  const int32_t* trow = a.tables + static_cast<int64_t>(it.b) * a.mb;
+  for (int t0 = it.tok0 + wave * kStep; t0 < it.tok1; t0 += kWaves * kStep) {
+    int blkA, blkB;
+    step_blocks<BS>(trow, t0, it.tok1, a.nb, blkA, blkB);
+    eng.step(pool, a.blk_elems, kofs, vofs, blkA, blkB, t0, it.tok1, lane, a.sl2e);
+  }
+  const float lt = sum_over_groups(eng.l[0]);
+  if (kg == 0) {
+    sm.m[wave][r] = eng.m[0];
+    sm.l[wave][r] = lt;
+  }
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j)
+    *reinterpret_cast<f32x4*>(&sm.o[wave][r][16 * j + 4 * kg]) = eng.o[0][j];
+  __syncthreads();
+
+  const int64_t row0 = static_cast<int64_t>(it.b) * a.hq + it.g * G;
+  finish_partition<D, uint16_t>(sm, G, it.np, it.p, a.np_max,
+                                static_cast<uint16_t*>(a.out) + row0 * D,
+                                a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2,
+                                a.ws_cnt + (static_cast<int64_t>(it.b) * a.hkv + it.g));
+}
+
+template <int D, int BS, int G>
+__global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
+  DecodeItem it;
+  if (!decode_item<BS>(a, it)) return;
+  __shared__ MergeSmem<D> sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = lane >> 4, c = lane & 15;
+  const float* pool = static_cast<const float*>(a.pool);
+  const float* q = static_cast<const float*>(a.q);
+  const int64_t row0 = static_cast<int64_t>(it.b) * a.hq + it.g * G;
+
+  F32Engine<D, BS, G> eng;
+  eng.init(q + row0 * D, c);
+  eng.lim = it.tok1 - 1;
+  const int64_t kofs = static_cast<int64_t>(it.g) * BS * D;
+  const int64_t vofs = static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(it.g) * D * BS;
+  const int32_t* trow = a.tables + static_cast<int64_t>(it.b) * a.mb;
+  for (int t0 = it.tok0 + wave * kStep; t0 < it.tok1; t0 += kWaves * kStep) {
+    int blkA, blkB;
+    step_blocks<BS>(trow, t0, it.tok1, a.nb, blkA, blkB);
+    eng.step(pool, a.blk_elems, kofs, vofs, blkA, blkB, t0, it.tok1, lane, a.sl2e);
+  }
+#pragma unroll
+  for (int qi = 0; qi < G; ++qi) {
+    const float lt = sum_over_groups(eng.l[qi]);
+#pragma unroll
+    for (int k = 0; k < F32Engine<D, BS, G>::EPL; ++k) {
+      const float v = sum_over_groups(eng.acc[qi][k]);
+      if (grp == 0) sm.o[wave][qi][c + 16 * k] = v;
+    }
+    if (lane == 0) {
+      sm.m[wave][qi] = eng.m[qi];
+      sm.l[wave][qi] = lt;
+    }
+  }
+  __syncthreads();
+  finish_partition<D, float>(sm, G, it.np, it.p, a.np_max, static_cast<float*>(a.out) + row0 * D,
+                             a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2,
+                             a.ws_cnt + (static_cast<int64_t>(it.b) * a.hkv + it.g));
+}
+
+// ---------------------------------------------------------------------------
+// Chunked prefill.
+// ---------------------------------------------------------------------------
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* pool;
+  const int32_t* tables;
+  const int32_t* lens;
+  const int32_t* qsl;
+  int num_chunks, total_q, mb, hq, hkv;
+  int64_t nb, blk_elems;
+  float sl2e;
+};
+
+// Chunk geometry: queries q0 .. q0+L-1 at positions prior .. prior+L-1.
+__device__ __forceinline__ bool chunk_geometry(const PrefillArgs& a, int c, int max_tokens, int& q0,
+                                               int& L, int& prior) {
+  q0 = a.qsl[c];
+  L = a.qsl[c + 1] - q0;
+  int n = a.lens[c];
+  n = n > max_tokens ? max_tokens : n;
+  if (q0 < 0 || L <= 0 || q0 + L > a.total_q || n < L) return false;
+  prior = n - L;
+  return true;
+}
+
+// bf16: a wave owns NT tiles of 16 rows; row R -> (position R / G, head R % G).
+template <int D, int BS, int NT>
+__global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
+  const int c = blockIdx.y, g = blockIdx.z;
+  int q0, L, prior;
+  if (!chunk_geometry(a, c, a.mb * BS, q0, L, prior)) return;
+  const int G = a.hq / a.hkv;
+  const int pos_per_wave = 16 * NT / G;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i0 = (blockIdx.x * kWaves + wave) * pos_per_wave;
+  if (i0 >= L) return;
+  const int r = lane & 15, kg = lane >> 4;
+  const uint16_t* pool = static_cast<const uint16_t*>(a.pool);
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+
+  Bf16Engine<D, BS, NT> eng;
+  eng.init();
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int R = nt * 16 + r;
+    const int i = i0 + R / G, h = R - (R / G) * G;
+    if (i < L) {
+      eng.load_q(nt, q + ((static_cast<int64_t>(q0) + i) * a.hq + g * G + h) * D, kg);
+      eng.lim[nt] = prior + i;
+    }
+  }
+  const int imax = min(L - 1, i0 + pos_per_wave - 1);
+  const int kend = prior + imax + 1;
+  const int64_t kofs = static_cast<int64_t>(g) * BS * D;
+  const int64_t vofs = static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(g) * D * BS;
+  const int32_t* trow = a.tables + static_cast<int64_t>(c) * a.mb;
+  for (int t0 = 0; t0 < kend; t0 += kStep) {
+    int blkA, blkB;
+    step_blocks<BS>(trow, t0, kend, a.nb, blkA, blkB);
+    eng.step(pool, a.blk_elems, kofs, vofs, blkA, blkB, t0, kend, lane, a.sl2e);
+  }
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float lt = sum_over_groups(eng.l[nt]);
+    const int R = nt * 16 + r;
+    const int i = i0 + R / G, h = R - (R / G) * G;
+    if (i >= L) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* orow = out + ((static_cast<int64_t>(q0) + i) * a.hq + g * G + h) * D;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      u32x2 w;
+      w[0] = f32_to_bf16_bits(eng.o[nt][j][0] * inv) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(eng.o[nt][j][1] * inv)) << 16);
+      w[1] = f32_to_bf16_bits(eng.o[nt][j][2] * inv) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(eng.o[nt][j][3] * inv)) << 16);
+      *reinterpret_cast<u32x2*>(orow + 16 * j + 4 * kg) = w;
+    }
+  }
+}
+
+// fp32: one workgroup per (position, chunk, kv head); its waves split the keys.
+template <int D, int BS, int G>
+__global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
+  const int i = blockIdx.x, c = blockIdx.y, g = blockIdx.z;
+  int q0, L, prior;
+  if (!chunk_geometry(a, c, a.mb * BS, q0, L, prior)) return;
+  if (i >= L) return;
+  __shared__ MergeSmem<D> sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = lane >> 4, cc = lane & 15;
+  const float* pool = static_cast<const float*>(a.pool);
+  const int64_t row0 = (static_cast<int64_t>(q0) + i) * a.hq + g * G;
+  F32Engine<D, BS, G> eng;
+  eng.init(static_cast<const float*>(a.q) + row0 * D, cc);
+  const int kend = prior + i + 1;
+  eng.lim = kend - 1;
+  const int64_t kofs = static_cast<int64_t>(g) * BS * D;
+  const int64_t vofs = static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(g) * D * BS;
+  const int32_t* trow = a.tables + static_cast<int64_t>(c) * a.mb;
+  for (int t0 = wave * kStep; t0 < kend; t0 += kWaves * kStep) {
+    int blkA, blkB;
+    step_blocks<BS>(trow, t0, kend, a.nb, blkA, blkB);
+    eng.step(pool, a.blk_elems, kofs, vofs, blkA, blkB, t0, kend, lane, a.sl2e);
+  }
+#pragma unroll
+  for (int qi = 0; qi < G; ++qi) {
+    const float lt = sum_over_groups(eng.l[qi]);
+#pragma unroll
+    for (int k = 0; k < F32Engine<D, BS, G>::EPL; ++k) {
+      const float v = sum_over_groups(eng.acc[qi][k]);
+      if (grp == 0) sm.o[wave][qi][cc + 16 * k] = v;
+    }
+    if (lane == 0) {
+      sm.m[wave][qi] = eng.m[qi];
+      sm.l[wave][qi] = lt;
+    }
+  }
+  __syncthreads();
+  finish_partition<D, float>(sm, G, 1, 0, 1, static_cast<float*>(a.out) + row0 * D, nullptr,
+                             nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// KV append and block copy (pure data movement).
+// ---------------------------------------------------------------------------
+// Thread -> (token, kv head, 8-element chunk). K: one contiguous 8-element run;
+// V: 8 elements spaced block_size apart in the dimension-major V half.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void append_kernel(T* __restrict__ pool,
+                                                     const T* __restrict__ kn,
+                                                     const T* __restrict__ vn,
+                                                     const int32_t* __restrict__ slots,
+                                                     int num_tokens, int hkv, int bs,
+                                                     int64_t blk_elems, int64_t num_slots) {
+  constexpr int CH = D / 8;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per_tok = static_cast<int64_t>(hkv) * CH;
+  const int64_t tok = gid / per_tok;
+  if (tok >= num_tokens) return;
+  const int rem = static_cast<int>(gid - tok * per_tok);
+  const int h = rem / CH, ch = rem - h * CH;
+  const int slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / bs;
+  const int off = slot - static_cast<int>(blk) * bs;
+  const int64_t src = (tok * hkv + h) * D + ch * 8;
+  T* kd = pool + blk * blk_elems + (static_cast<int64_t>(h) * bs + off) * D + ch * 8;
+  T* vd = pool + blk * blk_elems + static_cast<int64_t>(hkv) * bs * D +
+          (static_cast<int64_t>(h) * D + ch * 8) * bs + off;
+  constexpr int W = 8 * sizeof(T) / 16;  // 16-byte words per chunk
+#pragma unroll
+  for (int w = 0; w < W; ++w) st16(kd + w * (16 / sizeof(T)), ld16(kn + src + w * (16 / sizeof(T))));
+  T v[8];
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const u32x4 x = ld16(vn + src + w * (16 / sizeof(T)));
+    *reinterpret_cast<u32x4*>(&v[w * (16 / sizeof(T))]) = x;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vd[static_cast<int64_t>(e) * bs] = v[e];
+}
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ pool,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int64_t blk_bytes, int64_t nb) {
+  const int pi = blockIdx.y;
+  const int src = pairs[2 * pi], dst = pairs[2 * pi + 1];
+  if (static_cast<uint32_t>(src) >= static_cast<uint64_t>(nb) ||
+      static_cast<uint32_t>(dst) >= static_cast<uint64_t>(nb))
+    return;
+  const u32x4* s = reinterpret_cast<const u32x4*>(pool + src * blk_bytes);
+  u32x4* d = reinterpret_cast<u32x4*>(pool + dst * blk_bytes);
+  const int64_t n16 = blk_bytes / 16;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a0 = s[i], a1 = s[i + stride], a2 = s[i + 2 * stride], a3 = s[i + 3 * stride];
+    d[i] = a0;
+    d[i + stride] = a1;
+    d[i + 2 * stride] = a2;
+    d[i + 3 * stride] = a3;
+  }
+  for (; i < n16; i += stride) d[i] = s[i];
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch helpers.
+// ---------------------------------------------------------------------------
+template <int D, int BS>
+hipError_t launch_decode_bf16(const DecodeArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((decode_bf16_kernel<D, BS>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int BS>
+hipError_t launch_decode_f32(const DecodeArgs& a, int G, int grid, hipStream_t st) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((decode_f32_kernel<D, BS, 1>), dim3(grid), dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((decode_f32_kernel<D, BS, 2>), dim3(grid), dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((decode_f32_kernel<D, BS, 4>), dim3(grid), dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((decode_f32_kernel<D, BS, 8>), dim3(grid), dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+constexpr int kPrefillNT = 2;
+
+template <int D, int BS>
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int max_chunk_len, hipStream_t st) {
+  const int G = a.hq / a.hkv;
+  const int pos_per_wg = kWaves * 16 * kPrefillNT / G;
+  dim3 grid((max_chunk_len + pos_per_wg - 1) / pos_per_wg, a.num_chunks, a.hkv);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, BS, kPrefillNT>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int BS>
+hipError_t launch_prefill_f32(const PrefillArgs& a, int max_chunk_len, hipStream_t st) {
+  const int G = a.hq / a.hkv;
+  dim3 grid(max_chunk_len, a.num_chunks, a.hkv);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((prefill_f32_kernel<D, BS, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_f32_kernel<D, BS, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_f32_kernel<D, BS, 4>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((prefill_f32_kernel<D, BS, 8>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers (shapes already validated by the caller).
+// ---------------------------------------------------------------------------
+hipError_t launch_append(void* pool, const void* k_new, const void* v_new, const int32_t* slots,
+                         int num_tokens, const PoolShape& ps, int dtype, hipStream_t st) {
+  if (num_tokens == 0) return hipSuccess;
+  const int64_t threads = static_cast<int64_t>(num_tokens) * ps.num_kv_heads * (ps.head_dim / 8);
+  const int grid = static_cast<int>((threads + 255) / 256);
+  const int64_t num_slots = ps.num_blocks * ps.block_size;
+  const int64_t be = ps.block_elems();
+#define PA_APPEND(T, D)                                                                       \
+  hipLaunchKernelGGL((append_kernel<T, D>), dim3(grid), dim3(256), 0, st, static_cast<T*>(pool), \
+                     static_cast<const T*>(k_new), static_cast<const T*>(v_new), slots,          \
+                     num_tokens, ps.num_kv_heads, ps.block_size, be, num_slots)
+  if (dtype == 0) {
+    if (ps.head_dim == 64) PA_APPEND(float, 64); else PA_APPEND(float, 128);
+  } else {
+    if (ps.head_dim == 64) PA_APPEND(uint16_t, 64); else PA_APPEND(uint16_t, 128);
+  }
+#undef PA_APPEND
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(void* pool, const int32_t* pairs, int num_pairs, const PoolShape& ps,
+                       int dtype, hipStream_t st) {
+  if (num_pairs == 0) return hipSuccess;
+  const int64_t blk_bytes = ps.block_elems() * (dtype == 0 ? 4 : 2);
+  const int64_t n16 = blk_bytes / 16;
+  int gx = static_cast<int>((n16 + 1023) / 1024);  // about 4 x 16 B per thread
+  gx = gx < 1 ? 1 : gx;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, num_pairs), dim3(256), 0, st,
+                     static_cast<uint8_t*>(pool), pairs, blk_bytes, ps.num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(void* out, const void* q, const void* pool, const int32_t* tables,
+                         const int32_t* lens, int num_seqs, int max_blocks_per_seq,
+                         int max_context_len, int num_q_heads, const PoolShape& ps, float scale,
+                         int dtype, void* workspace, hipStream_t st) {
+  if (num_seqs == 0) return hipSuccess;
+  const int64_t np_max = decode_max_parts(max_context_len);
+  const DecodeWorkspace wl = DecodeWorkspace::layout(num_seqs, num_q_heads, ps.head_dim, np_max);
+  DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.pool = pool;
+  a.tables = tables;
+  a.lens = lens;
+  a.num_seqs = num_seqs;
+  a.mb = max_blocks_per_seq;
+  a.hq = num_q_heads;
+  a.hkv = ps.num_kv_heads;
+  a.max_ctx = max_context_len;
+  a.np_max = static_cast<int>(np_max);
+  a.nb = ps.num_blocks;
+  a.blk_elems = ps.block_elems();
+  a.sl2e = scale * kLog2e;
+  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+  a.ws_cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.cnt_off);
+  const int64_t items = static_cast<int64_t>(num_seqs) * ps.num_kv_heads * np_max;
+  a.n_items = static_cast<int>(items);
+  const int grid = static_cast<int>((items + 7) / 8 * 8);
+  const int G = num_q_heads / ps.num_kv_heads;
+  const int D = ps.head_dim, BS = ps.block_size;
+  if (dtype == 1) {
+    if (D == 64 && BS == 16) return launch_decode_bf16<64, 16>(a, grid, st);
+    if (D == 64 && BS == 32) return launch_decode_bf16<64, 32>(a, grid, st);
+    if (D == 128 && BS == 16) return launch_decode_bf16<128, 16>(a, grid, st);
+    if (D == 128 && BS == 32) return launch_decode_bf16<128, 32>(a, grid, st);
+  } else {
+    if (D == 64 && BS == 16) return launch_decode_f32<64, 16>(a, G, grid, st);
+    if (D == 64 && BS == 32) return launch_decode_f32<64, 32>(a, G, grid, st);
+    if (D == 128 && BS == 16) return launch_decode_f32<128, 16>(a, G, grid, st);
+    if (D == 128 && BS == 32) return launch_decode_f32<128, 32>(a, G, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(void* out, const void* q, const void* pool, const int32_t* tables,
+                          const int32_t* lens, const int32_t* qsl, int num_chunks,
+                          int total_q_tokens, int max_chunk_len, int max_blocks_per_seq,
+                          int num_q_heads,
+                          const PoolShape& ps, float scale, int dtype, hipStream_t st) {
+  if (num_chunks == 0 || max_chunk_len == 0) return hipSuccess;
+  PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.pool = pool;
+  a.tables = tables;
+  a.lens = lens;
+  a.qsl = qsl;
+  a.num_chunks = num_chunks;
+  a.total_q = total_q_tokens;
+  a.mb = max_blocks_per_seq;
+  a.hq = num_q_heads;
+  a.hkv = ps.num_kv_heads;
+  a.nb = ps.num_blocks;
+  a.blk_elems = ps.block_elems();
+  a.sl2e = scale * kLog2e;
+  const int D = ps.head_dim, BS = ps.block_size;
+  if (dtype == 1) {
+    if (D == 64 && BS == 16) return launch_prefill_bf16<64, 16>(a, max_chunk_len, st);
+    if (D == 64 && BS == 32) return launch_prefill_bf16<64, 32>(a, max_chunk_len, st);
+    if (D == 128 && BS == 16) return launch_prefill_bf16<128, 16>(a, max_chunk_len, st);
+    if (D == 128 && BS == 32) return launch_prefill_bf16<128, 32>(a, max_chunk_len, st);
+  } else {
+    if (D == 64 && BS == 16) return launch_prefill_f32<64, 16>(a, max_chunk_len, st);
+    if (D == 64 && BS == 32) return launch_prefill_f32<64, 32>(a, max_chunk_len, st);
+    if (D == 128 && BS == 16) return launch_prefill_f32<128, 16>(a, max_chunk_len, st);
+    if (D == 128 && BS == 32) return launch_prefill_f32<128, 32>(a, max_chunk_len, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

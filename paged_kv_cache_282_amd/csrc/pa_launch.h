@@ -1,0 +1,63 @@
+// Internal interface between the host API (pa_api.cpp) and the device code
+// (pa_kernels.hip). Arguments are validated by the caller; these functions only
+// size grids and launch on `stream`. Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kPartition = 512;   // split-K partition (tokens), see PA_DECODE_PARTITION
+constexpr int kWaves = 4;         // waves per workgroup in the attention kernels
+constexpr int kStep = 32;         // tokens per wave step
+
+struct PoolShape {
+  int64_t num_blocks;
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+  int64_t block_elems() const { return 2LL * num_kv_heads * block_size * head_dim; }
+};
+
+// Workspace carve-up for pa_decode (all offsets 256-byte aligned).
+struct DecodeWorkspace {
+  size_t o_off, ml_off, cnt_off, total;
+  static DecodeWorkspace layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
+                                int64_t max_parts) {
+    auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+    DecodeWorkspace w;
+    w.o_off = 0;
+    size_t o_bytes = size_t(num_seqs) * num_q_heads * max_parts * head_dim * sizeof(float);
+    w.ml_off = up(o_bytes);
+    size_t ml_bytes = size_t(num_seqs) * num_q_heads * max_parts * 2 * sizeof(float);
+    w.cnt_off = w.ml_off + up(ml_bytes);
+    size_t cnt_bytes = size_t(num_seqs) * num_q_heads * sizeof(int32_t);
+    w.total = w.cnt_off + up(cnt_bytes);
+    return w;
+  }
+};
+
+inline int64_t decode_max_parts(int64_t max_context_len) {
+  int64_t p = (max_context_len + kPartition - 1) / kPartition;
+  return p < 1 ? 1 : p;
+}
+
+hipError_t launch_append(void* pool, const void* k_new, const void* v_new, const int32_t* slots,
+                         int num_tokens, const PoolShape& ps, int dtype, hipStream_t stream);
+
+hipError_t launch_copy(void* pool, const int32_t* pairs, int num_pairs, const PoolShape& ps,
+                       int dtype, hipStream_t stream);
+
+hipError_t launch_decode(void* out, const void* q, const void* pool, const int32_t* tables,
+                         const int32_t* lens, int num_seqs, int max_blocks_per_seq,
+                         int max_context_len, int num_q_heads, const PoolShape& ps, float scale,
+                         int dtype, void* workspace, hipStream_t stream);
+
+hipError_t launch_prefill(void* out, const void* q, const void* pool, const int32_t* tables,
+                          const int32_t* lens, const int32_t* qsl, int num_chunks,
+                          int total_q_tokens, int max_chunk_len, int max_blocks_per_seq, int num_q_heads,
+                          const PoolShape& ps, float scale, int dtype, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,312 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bars: KV append, block copy and everything the block table decides are
+bit-exact (the whole pool is compared bitwise after each step); attention
+outputs are within max abs error 1e-5 (float32) and 2e-2 (bfloat16 with
+float32 accumulation). Invariants that hold exactly on the GPU (single-token
+contexts, block relabelling, shared vs duplicated blocks, GQA vs repeated MHA,
+batch composition) are checked bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_helpers import (TOL, DeviceStep, bits, i32, max_err, oracle_decode,
+                               oracle_pool_after, oracle_prefill, to_dev, values)
+from tests.pool_writer import unshare_blocks
+from workloads import build_decode_workload, make_workload
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny": dict(),
+    "mha": dict(num_seqs=12, min_len=1, max_len=1300, num_heads=4),
+    "gqa": dict(num_seqs=24, median=300, hi=2100, num_q_heads=16, num_kv_heads=2),
+    "prefix": dict(num_prompts=3, samples=4, prefix_len=1032, max_suffix=200, num_q_heads=8,
+                   num_kv_heads=2),
+    "mixed": dict(num_decode=10, dec_min=1, dec_max=1200, num_chunks=4, chunk_len=100,
+                  max_prior=700, num_q_heads=8, num_kv_heads=2),
+}
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _check_step(w, label):
+    _say(f"[case] {label}: B={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+         f"d={w.head_dim} bs={w.block_size} {w.dtype} max_ctx={w.max_context_len}")
+    st = DeviceStep(w)
+    st.run()
+    want_pool = oracle_pool_after(w)
+    got_pool = bits(st.pool)
+    assert np.array_equal(got_pool.view(np.uint8), want_pool.view(np.uint8)), \
+        "pool after copy+append differs from the oracle"
+    err = max_err(values(st.out), oracle_decode(w, want_pool))
+    _say(f"  decode max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+    if w.prefill_q is not None:
+        perr = max_err(values(st.pout), oracle_prefill(w, want_pool))
+        _say(f"  prefill max abs err {perr:.3e}")
+        assert perr <= TOL[w.dtype]
+    return st
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_step_parity_small(name, dtype):
+    w = make_workload(name, dtype=dtype, **SMALL[name])
+    _check_step(w, f"{name}-small")
+
+
+@pytest.mark.parametrize("name", ["tiny", "mha", "gqa", "prefix", "mixed"])
+def test_step_parity_full_size(name):
+    """Every output of the full-size workloads against the oracle."""
+    w = make_workload(name)
+    _check_step(w, f"{name}-full")
+
+
+@pytest.mark.parametrize("name", ["mha", "gqa"])
+def test_float32_at_full_shapes(name):
+    """float32 inputs at the full shapes: a 1e-5 bound discriminates far more than 2e-2."""
+    w = make_workload(name, dtype="f32")
+    _check_step(w, f"{name}-full-f32")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_shape_matrix(dtype, d, bs, G):
+    """Edge lengths around blocks, steps and the 512-token partition."""
+    lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1024, 1025, 1537]
+    w = build_decode_workload("matrix", 1000 + d + bs + G, lens, 2 * G, 2, d, bs, dtype)
+    _check_step(w, f"matrix-{dtype}-d{d}-bs{bs}-G{G}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_shape_matrix(dtype, d, bs, G):
+    w = make_workload("mixed", dtype=dtype, seed=2000 + d + bs + G, num_decode=3, dec_min=1,
+                      dec_max=100, num_chunks=5, chunk_len=37, max_prior=300,
+                      num_q_heads=2 * G, num_kv_heads=2, head_dim=d, block_size=bs)
+    _check_step(w, f"prefill-{dtype}-d{d}-bs{bs}-G{G}")
+
+
+def test_prefill_ragged_chunks():
+    """Chunks of lengths 1, 5, 64 and 130 in one call (each the last L of its context)."""
+    w = make_workload("mixed", num_decode=2, num_chunks=4, chunk_len=130, max_prior=200,
+                      num_q_heads=8, num_kv_heads=2, dec_max=300)
+    lens = [1, 5, 64, 130]
+    q, qsl, ctx = [], [0], []
+    for c, L in enumerate(lens):
+        lo = int(w.query_start_loc[c])
+        q.append(w.prefill_q[lo:lo + L])
+        qsl.append(qsl[-1] + L)
+        ctx.append(int(w.prefill_context_lens[c]) - 130 + L)
+    w.prefill_q = np.concatenate(q)
+    w.query_start_loc = np.array(qsl, np.int32)
+    w.prefill_context_lens = np.array(ctx, np.int32)
+    _check_step(w, "prefill-ragged")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_token_context_returns_v_bit_exactly(dtype):
+    w = build_decode_workload("one", 7, [1] * 9, 8, 2, 128, 16, dtype)
+    st = DeviceStep(w)
+    st.run()
+    G = 4
+    want = w.v_new[:, np.arange(8) // G, :]  # [B][Hq][d] storage
+    assert np.array_equal(bits(st.out), want)
+
+
+def test_block_relabelling_is_bit_invariant():
+    w = make_workload("gqa", **SMALL["gqa"])
+    st = DeviceStep(w)
+    st.run()
+    base = bits(st.out).copy()
+    pool_after = bits(st.pool)
+    perm = np.random.default_rng(5).permutation(w.num_blocks)
+    new_pool = np.empty_like(pool_after)
+    new_pool[perm] = pool_after
+    st2 = DeviceStep(w)
+    st2.pool = to_dev(new_pool, w.dtype)
+    st2.tables = i32(perm[w.block_tables])
+    st2.decode()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(st2.out), base)
+
+
+def test_shared_prefix_equals_duplicated_bitwise():
+    w = make_workload("prefix", **SMALL["prefix"])
+    st = DeviceStep(w)
+    st.run()
+    shared = bits(st.out).copy()
+    p2, t2 = unshare_blocks(bits(st.pool), w.block_tables, w.context_lens, w.block_size,
+                            w.poison_block)
+    st.pool = to_dev(p2, w.dtype)
+    st.tables = i32(t2)
+    st.decode()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(st.out), shared)
+
+
+def test_gqa_equals_mha_with_repeated_heads_bitwise():
+    w = make_workload("gqa", num_seqs=9, median=400, hi=1500, num_q_heads=8, num_kv_heads=2)
+    st = DeviceStep(w)
+    st.run()
+    gqa = bits(st.out).copy()
+    pool = bits(st.pool)
+    nb = pool.shape[0]
+    rep = np.repeat(pool.reshape(nb, 2, 2, -1), 4, axis=2).reshape(nb, -1)
+    st.pool = to_dev(rep, w.dtype)
+    st.ws = torch.zeros_like(st.ws)
+    import paged_kv_cache_282_amd as pa
+    pa.pa_decode(st.out, st.q, st.pool, st.tables, st.lens, w.max_context_len, 8,
+                 w.block_size, w.scale, pa.new_decode_workspace(w.num_seqs, 8, w.head_dim,
+                                                                w.max_context_len))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(st.out), gqa)
+
+
+def test_batch_composition_is_bit_invariant():
+    w = make_workload("gqa", **SMALL["gqa"])
+    st = DeviceStep(w)
+    st.run()
+    full = bits(st.out).copy()
+    order = np.array([17, 3, 3, 22, 0, 9])  # subset, reordered, with a repeat
+    import paged_kv_cache_282_amd as pa
+    out = torch.empty((len(order), w.num_q_heads, w.head_dim), dtype=st.q.dtype, device="cuda")
+    sub_max = int(w.context_lens[order].max())
+    pa.pa_decode(out, st.q[torch.from_numpy(order).cuda()].contiguous(), st.pool,
+                 st.tables[torch.from_numpy(order).cuda()].contiguous(),
+                 st.lens[torch.from_numpy(order).cuda()].contiguous(), sub_max, w.num_kv_heads,
+                 w.block_size, w.scale,
+                 pa.new_decode_workspace(len(order), w.num_q_heads, w.head_dim, sub_max))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), full[order])
+
+
+def test_prefill_chunk_of_one_matches_decode():
+    w = make_workload("mixed", num_decode=2, dec_max=300, num_chunks=6, chunk_len=1,
+                      max_prior=1500, num_q_heads=8, num_kv_heads=2)
+    st = DeviceStep(w)
+    st.run()
+    import paged_kv_cache_282_amd as pa
+    dec = torch.empty_like(st.pq)
+    mx = int(w.prefill_context_lens.max())
+    pa.pa_decode(dec, st.pq, st.pool, st.ptables, st.plens, mx, w.num_kv_heads, w.block_size,
+                 w.scale, pa.new_decode_workspace(6, w.num_q_heads, w.head_dim, mx))
+    torch.cuda.synchronize()
+    want = oracle_prefill(w, oracle_pool_after(w))
+    assert max_err(values(st.pout), want) <= TOL["bf16"]
+    assert max_err(values(dec), want) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sharpened_queries(dtype):
+    """q scaled x8: a peaked softmax makes o close to single V rows, so a wrong
+    block or slot moves the output by O(1)."""
+    w = make_workload("gqa", dtype=dtype, **SMALL["gqa"])
+    if dtype == "f32":
+        w.q = (w.q * 8).astype(np.float32)
+    else:
+        f = (w.q.astype(np.uint32) << 16).view(np.float32) * 8  # exact: power of two
+        w.q = (f.view(np.uint32) >> 16).astype(np.uint16)
+    _check_step(w, f"sharpened-{dtype}")
+
+
+def test_zero_length_contexts_give_zero_rows():
+    w = build_decode_workload("z", 3, [5, 600, 40], 4, 2, 128, 16, "bf16")
+    st = DeviceStep(w)
+    st.copy()
+    st.append()
+    st.lens = i32([0, 600, 0])
+    st.out.fill_(1.0)
+    st.decode()
+    torch.cuda.synchronize()
+    out = values(st.out)
+    assert (out[0] == 0).all() and (out[2] == 0).all()
+    w.context_lens = np.array([0, 600, 0], np.int32)
+    want = oracle_decode(w, oracle_pool_after(w))
+    assert max_err(out, want) <= TOL["bf16"]
+
+
+def test_empty_batch_is_a_no_op():
+    import paged_kv_cache_282_amd as pa
+    pool = torch.zeros(2 * 2 * 16 * 64 * 4, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    tables = torch.zeros((0, 1), dtype=torch.int32, device="cuda")
+    lens = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(1, dtype=torch.uint8, device="cuda")
+    pa.pa_decode(out, q, pool, tables, lens, 0, 2, 16, 0.125, ws)
+    pa.pa_append_kv(pool, torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda"),
+                    torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda"),
+                    torch.zeros((0,), dtype=torch.int32, device="cuda"), 16)
+    torch.cuda.synchronize()
+    assert (pool == 0).all()
+
+
+def test_repeated_calls_reuse_workspace_and_are_deterministic():
+    """Bit-identical reruns; the workspace's split-K counters return to zero, so a
+    different batch can reuse it."""
+    import paged_kv_cache_282_amd as pa
+    a = make_workload("gqa", **SMALL["gqa"])
+    b = make_workload("mha", num_seqs=10, min_len=600, max_len=3000, num_heads=4)
+    ws = pa.new_decode_workspace(24, 16, 128, 3000)
+    sa = DeviceStep(a)
+    sa.ws = ws
+    sa.run()
+    first = bits(sa.out).copy()
+    for _ in range(3):
+        sa.out.zero_()
+        sa.decode()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(sa.out), first)
+    sb = DeviceStep(b)
+    sb.ws = ws
+    sb.run()
+    assert max_err(values(sb.out), oracle_decode(b, oracle_pool_after(b))) <= TOL["bf16"]
+
+
+def test_output_is_convex_combination():
+    w = make_workload("gqa", **SMALL["gqa"])
+    st = DeviceStep(w)
+    st.run()
+    out = values(st.out)
+    import oracle
+    pool = oracle_pool_after(w)
+    G = w.num_q_heads // w.num_kv_heads
+    for b in range(w.num_seqs):
+        for h in range(w.num_q_heads):
+            _, V = oracle.gather(pool, w.dtype, w.block_tables[b], int(w.context_lens[b]),
+                                 h // G, w.num_kv_heads, w.block_size, w.head_dim)
+            lo, hi = V.min(0), V.max(0)
+            slack = 2.0 ** -7 * np.maximum(np.abs(lo), np.abs(hi))  # bf16 output rounding
+            assert (out[b, h] >= lo - slack).all() and (out[b, h] <= hi + slack).all()
+
+
+def test_high_block_ids_use_64bit_offsets():
+    """Blocks whose element offsets exceed 2^31 (a pool above 4 GiB of bf16)."""
+    w = make_workload("gqa", num_seqs=6, median=300, hi=1200, num_q_heads=16, num_kv_heads=2)
+    be = w.block_elems
+    base = (2 ** 31) // be + 7  # first block id whose offset exceeds 2^31 elements
+    nb_big = base + w.num_blocks
+    _say(f"[case] 64-bit offsets: pool of {nb_big} blocks = {nb_big * be * 2 / 2**30:.2f} GiB")
+    st = DeviceStep(w)
+    big = torch.full((nb_big * be,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    big[base * be:] = st.pool
+    st.pool = big
+    st.tables = i32(w.block_tables + base)
+    st.slots = i32(w.slot_mapping.astype(np.int64) + base * w.block_size)
+    st.append()
+    st.decode()
+    torch.cuda.synchronize()
+    want_pool = oracle_pool_after(w)
+    assert np.array_equal(bits(st.pool[base * be:]).reshape(want_pool.shape), want_pool)
+    assert max_err(values(st.out), oracle_decode(w, want_pool)) <= TOL["bf16"]
+    del big, st
+    torch.cuda.empty_cache()
