@@ -141,10 +141,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  *   max_context_len  host-side upper bound of context_lens (sizes the grid).
  *   scale         multiplies q.K (1/sqrt(head_dim) for standard attention).
  *   workspace     device buffer of at least pa_decode_workspace_size() bytes,
- *                 ZERO-FILLED before its first use. Each call leaves it ready
- *                 for the next call (its counters return to zero), so it can
- *                 be reused across calls and layers; calls that may run
- *                 concurrently need separate workspaces.
+ *                 ZERO-FILLED before its first use. It holds work-queue
+ *                 counters, which every call returns to zero, and partial
+ *                 results. The counters' place does not depend on the batch
+ *                 shape, so one workspace serves any sequence of calls on one
+ *                 stream; calls that may run concurrently need separate
+ *                 workspaces.
+ * Sequences longer than PA_DECODE_PARTITION are split into partitions whose
+ * partial softmax states are merged by a second kernel on the same stream.
  */
 int pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
               const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,

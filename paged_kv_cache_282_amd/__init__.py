@@ -155,7 +155,7 @@ def new_decode_workspace(num_seqs: int, num_q_heads: int, head_dim: int, max_con
                          device="cuda") -> torch.Tensor:
     """A zero-filled workspace of the size pa_decode needs."""
     n = pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len)
-    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len: int,

@@ -110,6 +110,7 @@ int pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* bloc
   if (int64_t(max_context_len) > int64_t(max_blocks_per_seq) * block_size) return PA_ERR_SHAPE;
   const int64_t parts = pa::decode_max_parts(max_context_len);
   if (int64_t(num_seqs) * num_kv_heads * parts > (int64_t(1) << 30)) return PA_ERR_SHAPE;
+  if (int64_t(num_seqs) * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;  // merge grid
   if (workspace_bytes < pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len))
     return PA_ERR_WORKSPACE;
   const size_t qbytes = size_t(num_seqs) * num_q_heads * head_dim * elem_bytes(dtype);

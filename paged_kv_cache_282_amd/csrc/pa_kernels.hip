@@ -43,6 +43,12 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Four floats as a float vector. (Reading float lanes out of an integer vector
+// with __builtin_bit_cast on a vector element is avoided on purpose: clang
+// lowers that to a read of element 0.)
+__device__ __forceinline__ f32x4 ld16f(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -74,14 +80,6 @@ __device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
 template <>
 __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
   *p = f32_to_bf16_bits(v);
-}
-
-// Workgroups are dispatched round-robin over the 8 XCDs of the chip. Giving
-// each XCD a contiguous range of logical items keeps the partitions of one
-// (sequence, kv head) -- and the merge that reads them -- on one L2.
-__device__ __forceinline__ int xcd_remap(int wid, int nwg) {
-  const int per = nwg >> 3;  // nwg is a multiple of 8
-  return (wid & 7) * per + (wid >> 3);
 }
 
 __device__ __forceinline__ int clamp_block(int blk, int64_t nb) {
@@ -134,13 +132,19 @@ struct Bf16Engine {
       qreg[nt][s] = __builtin_bit_cast(bf16x8, ld16(q_row + 32 * s + 8 * kg));
   }
 
-  // One 32-token step starting at logical token t0. Tokens t0..t0+15 live in
-  // block blkA and t0+16..t0+31 in blkB (bs 16) or all in blkA (bs 32).
-  // Tokens >= vend have their V zeroed (they may be NaN); scores of tokens past
-  // a row's limit are -inf.
-  __device__ __forceinline__ void step(const uint16_t* __restrict__ pool, int64_t blk_elems,
-                                       int64_t kofs, int64_t vofs, int blkA, int blkB, int t0,
-                                       int vend, int lane, float sl2e) {
+  // Registers of one 32-token step: K rows of the two score sets and V^T.
+  struct KV {
+    u32x4 kA[KS], kB[KS], vv[VT];
+  };
+
+  // Issue the loads of a 32-token step. Tokens t0..t0+15 live in block blkA
+  // and t0+16..t0+31 in blkB (bs 16) or all in blkA (bs 32).
+  __device__ __forceinline__ void load_kv(KV& kv, const uint16_t* __restrict__ pool,
+                                          int64_t blk_elems, int64_t kofs, int64_t vofs, int blkA,
+                                          int blkB, int lane, bool live = true) const {
+    // A step that will not be computed (live == false) still issues its loads,
+    // so that the number of loads in flight is the same on every path, but
+    // every lane reads the same 16 bytes: one cache line per instruction.
     const int r = lane & 15, kg = lane >> 4;
     const uint16_t* baseA = pool + static_cast<int64_t>(blkA) * blk_elems;
     const uint16_t* baseB = pool + static_cast<int64_t>(blkB) * blk_elems;
@@ -160,16 +164,26 @@ struct Bf16Engine {
       vp = (kg < 2 ? baseA : baseB) + vofs + 8 * (kg & 1);
     else
       vp = baseA + vofs + 8 * kg;
-
-    u32x4 kA[KS], kB[KS], vv[VT];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kA[s] = ld16(ka + 32 * s);
-      kB[s] = ld16(kb + 32 * s);
+    const int ks = live ? 32 : 0;
+    const int vs = live ? BS : 0;
+    if (!live) {
+      ka = pool;
+      kb = pool;
+      vp = pool;
     }
 #pragma unroll
-    for (int j = 0; j < VT; ++j) vv[j] = ld16(vp + (16 * j + r) * BS);
+    for (int s = 0; s < KS; ++s) {
+      kv.kA[s] = ld16(ka + ks * s);
+      kv.kB[s] = ld16(kb + ks * s);
+    }
+#pragma unroll
+    for (int j = 0; j < VT; ++j) kv.vv[j] = ld16(vp + (16 * j + r) * vs);
+  }
 
+  // Consume a loaded step starting at token t0. Tokens >= vend have their V
+  // zeroed (they may be NaN); scores of tokens past a row's limit are -inf.
+  __device__ __forceinline__ void compute(KV& kv, int t0, int vend, int lane, float sl2e) {
+    const int kg = lane >> 4;
     if (t0 + 32 > vend) {  // wave-uniform: zero V of tokens past the end
       const int nvalid = vend - t0 - 8 * kg;
 #pragma unroll
@@ -177,19 +191,18 @@ struct Bf16Engine {
         const uint32_t mask = (2 * w < nvalid ? 0x0000FFFFu : 0u) |
                               (2 * w + 1 < nvalid ? 0xFFFF0000u : 0u);
 #pragma unroll
-        for (int j = 0; j < VT; ++j) vv[j][w] &= mask;
+        for (int j = 0; j < VT; ++j) kv.vv[j][w] &= mask;
       }
     }
-
     const int tbase = t0 + 8 * kg;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kA[s]),
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv.kA[s]),
                                                      qreg[nt][s], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kB[s]),
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv.kB[s]),
                                                      qreg[nt][s], sb, 0, 0, 0);
       }
       float sc[8];
@@ -221,10 +234,18 @@ struct Bf16Engine {
 #pragma unroll
       for (int j = 0; j < VT; ++j) {
         o[nt][j] *= alpha;
-        o[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv[j]), p,
-                                                           o[nt][j], 0, 0, 0);
+        o[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv.vv[j]),
+                                                           p, o[nt][j], 0, 0, 0);
       }
     }
+  }
+
+  __device__ __forceinline__ void step(const uint16_t* __restrict__ pool, int64_t blk_elems,
+                                       int64_t kofs, int64_t vofs, int blkA, int blkB, int t0,
+                                       int vend, int lane, float sl2e) {
+    KV kv;
+    load_kv(kv, pool, blk_elems, kofs, vofs, blkA, blkB, lane);
+    compute(kv, t0, vend, lane, sl2e);
   }
 };
 
@@ -278,9 +299,9 @@ struct F32Engine {
       float kv[EPL];
 #pragma unroll
       for (int k4 = 0; k4 < EPL / 4; ++k4) {
-        const u32x4 w = ld16(kr + 4 * k4);
+        const f32x4 w = ld16f(kr + 4 * k4);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) kv[4 * k4 + x] = __builtin_bit_cast(float, w[x]);
+        for (int x = 0; x < 4; ++x) kv[4 * k4 + x] = w[x];
       }
       const bool valid = tbase + e <= lim;
 #pragma unroll
@@ -317,11 +338,11 @@ struct F32Engine {
     for (int k = 0; k < EPL; ++k) {
       const float* vr = base + vofs + (c + 16 * k) * BS + slot0;
       float v[8];
-      const u32x4 w0 = ld16(vr), w1 = ld16(vr + 4);
+      const f32x4 w0 = ld16f(vr), w1 = ld16f(vr + 4);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        v[x] = __builtin_bit_cast(float, w0[x]);
-        v[4 + x] = __builtin_bit_cast(float, w1[x]);
+        v[x] = w0[x];
+        v[4 + x] = w1[x];
       }
       if (tail) {
 #pragma unroll
@@ -338,12 +359,13 @@ struct F32Engine {
 // ---------------------------------------------------------------------------
 // Workgroup-level merge of the per-wave states held in LDS.
 // ---------------------------------------------------------------------------
+constexpr int kMaxGroup = 8;  // query heads per kv head handled by the decode kernels
+
 template <int D>
 struct MergeSmem {
-  float o[kWaves][16][D];
-  float m[kWaves][16];
-  float l[kWaves][16];
-  int last;
+  float o[kWaves][kMaxGroup][D];
+  float m[kWaves][kMaxGroup];
+  float l[kWaves][kMaxGroup];
 };
 
 // Combines the kWaves states of row `row` at dimension `dd`: (M, L, O).
@@ -364,61 +386,29 @@ __device__ __forceinline__ void combine_waves(const MergeSmem<D>& sm, int row, i
   }
 }
 
-// After each wave has written its state, either store the normalised output
-// (single partition) or publish this partition's state and let the last
-// partition to finish merge all of them.
+// After each wave has written its state: a single-partition sequence stores
+// its normalised output; otherwise this partition publishes (M, L, O) for the
+// merge kernel.
 template <int D, typename OutT>
-__device__ __forceinline__ void finish_partition(MergeSmem<D>& sm, int rows, int np, int p,
+__device__ __forceinline__ void finish_partition(const MergeSmem<D>& sm, int rows, int np, int p,
                                                  int np_max, OutT* __restrict__ out_rows,
                                                  float* __restrict__ ws_o,
-                                                 float* __restrict__ ws_ml,
-                                                 int32_t* __restrict__ counter) {
+                                                 float* __restrict__ ws_ml) {
   // out_rows: rows * D outputs; ws_o / ws_ml: this (sequence, group)'s first
   // row's partials, rows spaced np_max * D (resp. np_max * 2) apart.
-  if (np == 1) {
-    for (int idx = threadIdx.x; idx < rows * D; idx += kWaves * 64) {
-      const int row = idx / D, dd = idx - row * D;
-      float M, L, O;
-      combine_waves<D>(sm, row, dd, M, L, O);
-      store_out<OutT>(out_rows + idx, L > 0.f ? O / L : 0.f);
-    }
-    return;
-  }
   for (int idx = threadIdx.x; idx < rows * D; idx += kWaves * 64) {
     const int row = idx / D, dd = idx - row * D;
     float M, L, O;
     combine_waves<D>(sm, row, dd, M, L, O);
-    ws_o[(static_cast<int64_t>(row) * np_max + p) * D + dd] = O;
-    if (dd == 0) {
-      ws_ml[(static_cast<int64_t>(row) * np_max + p) * 2 + 0] = M;
-      ws_ml[(static_cast<int64_t>(row) * np_max + p) * 2 + 1] = L;
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(counter, 1);
-    sm.last = (prev == np - 1);
-    if (prev == np - 1) atomicExch(counter, 0);  // ready for the next call
-  }
-  __syncthreads();
-  if (!sm.last) return;
-  __threadfence();
-  for (int idx = threadIdx.x; idx < rows * D; idx += kWaves * 64) {
-    const int row = idx / D, dd = idx - row * D;
-    const float* mlr = ws_ml + static_cast<int64_t>(row) * np_max * 2;
-    const float* orow = ws_o + static_cast<int64_t>(row) * np_max * D + dd;
-    float M = -__builtin_inff();
-    for (int pp = 0; pp < np; ++pp) M = fmaxf(M, mlr[2 * pp]);
-    float L = 0.f, O = 0.f;
-    if (M != -__builtin_inff()) {
-      for (int pp = 0; pp < np; ++pp) {
-        const float f = exp2_fast(mlr[2 * pp] - M);
-        L = fmaf(mlr[2 * pp + 1], f, L);
-        O = fmaf(orow[static_cast<int64_t>(pp) * D], f, O);
+    if (np == 1) {
+      store_out<OutT>(out_rows + idx, L > 0.f ? O / L : 0.f);
+    } else {
+      ws_o[(static_cast<int64_t>(row) * np_max + p) * D + dd] = O;
+      if (dd == 0) {
+        ws_ml[(static_cast<int64_t>(row) * np_max + p) * 2 + 0] = M;
+        ws_ml[(static_cast<int64_t>(row) * np_max + p) * 2 + 1] = L;
       }
     }
-    store_out<OutT>(out_rows + idx, L > 0.f ? O / L : 0.f);
   }
 }
 
@@ -433,19 +423,25 @@ struct DecodeArgs {
   float sl2e;
   float* ws_o;
   float* ws_ml;
-  int32_t* ws_cnt;
 };
 
 // Resolves (sequence, kv head, partition) of this workgroup; false if idle.
 struct DecodeItem {
   int b, g, p, np, tok0, tok1;
 };
+// Workgroup -> (sequence, kv head, partition). Items are ordered
+// partition-major: every sequence's first partition comes first, then every
+// second partition, and so on. Each item is at most one partition long, so
+// the hardware dispatcher balances them; the grid is sized for the longest
+// context and items past a sequence's last partition exit at once, in the
+// trailing part of the grid.
 template <int BS>
 __device__ __forceinline__ bool decode_item(const DecodeArgs& a, DecodeItem& it) {
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int item = blockIdx.x;
   if (item >= a.n_items) return false;
-  const int bg = item / a.np_max;
-  it.p = item - bg * a.np_max;
+  const int groups = a.num_seqs * a.hkv;
+  it.p = item / groups;
+  const int bg = item - it.p * groups;
   it.b = bg / a.hkv;
   it.g = bg - it.b * a.hkv;
   int n = a.lens[it.b];
@@ -500,20 +496,302 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     eng.step(pool, a.blk_elems, kofs, vofs, blkA, blkB, t0, it.tok1, lane, a.sl2e);
   }
   const float lt = sum_over_groups(eng.l[0]);
-  if (kg == 0) {
-    sm.m[wave][r] = eng.m[0];
-    sm.l[wave][r] = lt;
-  }
+  if (r < G) {
+    if (kg == 0) {
+      sm.m[wave][r] = eng.m[0];
+      sm.l[wave][r] = lt;
+    }
 #pragma unroll
-  for (int j = 0; j < D / 16; ++j)
-    *reinterpret_cast<f32x4*>(&sm.o[wave][r][16 * j + 4 * kg]) = eng.o[0][j];
+    for (int j = 0; j < D / 16; ++j)
+      *reinterpret_cast<f32x4*>(&sm.o[wave][r][16 * j + 4 * kg]) = eng.o[0][j];
+  }
   __syncthreads();
 
   const int64_t row0 = static_cast<int64_t>(it.b) * a.hq + it.g * G;
   finish_partition<D, uint16_t>(sm, G, it.np, it.p, a.np_max,
                                 static_cast<uint16_t*>(a.out) + row0 * D,
-                                a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2,
-                                a.ws_cnt + (static_cast<int64_t>(it.b) * a.hkv + it.g));
+                                a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent bf16 decode with a dynamic work queue (batches of up to
+// kMaxScanSeqs sequences).
+//
+// Every workgroup first scans the context lengths into LDS: per sequence the
+// number of full 512-token partitions and whether a shorter trailing one
+// follows. The work items -- (sequence, kv head, partition) -- are numbered
+// full partitions first, then the trailing partial ones, so the queue ends
+// with the smallest items. Workgroups take items from an atomic counter in the
+// workspace until it runs past the last item; the last workgroup to leave
+// returns the counters to zero for the next call. Nothing waits on another
+// workgroup.
+// ---------------------------------------------------------------------------
+constexpr int kMaxScanSeqs = 2048;
+
+struct ScanSmem {
+  int full[kMaxScanSeqs + 1];  // exclusive prefix: full partitions before sequence b
+  int part[kMaxScanSeqs + 1];  // exclusive prefix: trailing partial partitions before b
+  int n[kMaxScanSeqs];         // clamped context length
+  int wsum[kWaves][2];
+  int item;
+};
+
+template <int BS>
+__device__ __forceinline__ int clamped_len(const DecodeArgs& a, int b) {
+  int n = a.lens[b];
+  n = n < 0 ? 0 : n;
+  n = n > a.max_ctx ? a.max_ctx : n;
+  return n > a.mb * BS ? a.mb * BS : n;
+}
+
+// Exclusive block-wide scan (256 threads) of a pair of counts.
+__device__ __forceinline__ void block_scan2(ScanSmem& sc, int x, int y, int& ex, int& ey,
+                                            int& tx, int& ty) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int ix = x, iy = y;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int ox = __shfl_up(ix, d), oy = __shfl_up(iy, d);
+    if (lane >= d) {
+      ix += ox;
+      iy += oy;
+    }
+  }
+  if (lane == 63) {
+    sc.wsum[wave][0] = ix;
+    sc.wsum[wave][1] = iy;
+  }
+  __syncthreads();
+  int bx = 0, by = 0;
+  tx = 0;
+  ty = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) {
+      bx += sc.wsum[w][0];
+      by += sc.wsum[w][1];
+    }
+    tx += sc.wsum[w][0];
+    ty += sc.wsum[w][1];
+  }
+  ex = bx + ix - x;
+  ey = by + iy - y;
+}
+
+// Largest b in [0, B) with pre[b] <= j, for pre[0] <= j < pre[B].
+__device__ __forceinline__ int search_prefix(const int* pre, int B, int j) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= j) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// One queue item: (sequence b, kv head g, partition p) and its token range.
+struct QItem {
+  int b, g, p, np, tok0, tok1, nsteps;
+};
+
+__device__ __forceinline__ void resolve_item(const ScanSmem& sc, int B, int hkv, int n_full_items,
+                                             int k, QItem& it) {
+  if (k < n_full_items) {
+    const int j = k / hkv;
+    it.g = k - j * hkv;
+    it.b = search_prefix(sc.full, B, j);
+    it.p = j - sc.full[it.b];
+  } else {
+    const int k2 = k - n_full_items;
+    const int j = k2 / hkv;
+    it.g = k2 - j * hkv;
+    it.b = search_prefix(sc.part, B, j);
+    it.p = sc.full[it.b + 1] - sc.full[it.b];
+  }
+  const int n = sc.n[it.b];
+  it.np = (sc.full[it.b + 1] - sc.full[it.b]) + (sc.part[it.b + 1] - sc.part[it.b]);
+  it.tok0 = it.p * kPartition;
+  it.tok1 = min(n, it.tok0 + kPartition);
+  it.nsteps = (it.tok1 - it.tok0 + kStep - 1) / kStep;
+}
+
+// Items are processed as a pipeline. The queue runs two items ahead: while
+// item i computes, every wave already holds the block ids and query of item
+// i+1, and as soon as a wave finishes its steps of item i it issues the first
+// two steps of item i+1, so the workgroup barrier, merge and publish of item i
+// overlap memory traffic of item i+1.
+//
+// Every load of the step pipeline is issued unconditionally, in straight-line
+// code: a step past the end of its item (or a prefetch past the end of the
+// queue) reads block 0, which stays cached, and is never computed. Loads
+// inside branches would make the compiler's wait counts conservative (wait for
+// all outstanding loads), which serialises loads and compute.
+template <int D, int BS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
+  using Eng = Bf16Engine<D, BS, 1>;
+  constexpr int KS = Eng::KS;
+  constexpr int kSteps = kPartition / (kWaves * kStep);  // steps per wave per partition
+  static_assert(kSteps % 2 == 0, "steps alternate between two register buffers");
+  __shared__ MergeSmem<D> sm2[2];  // wave states of consecutive items alternate
+  __shared__ ScanSmem sc;
+  __shared__ int s_next[2];
+  const int B = a.num_seqs;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, kg = lane >> 4;
+  const int G = a.hq / a.hkv;
+  const uint16_t* pool = static_cast<const uint16_t*>(a.pool);
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+
+  // -- scan the lengths; take the first two items ---------------------------------
+  {
+    constexpr int kPer = kMaxScanSeqs / 256;
+    const int per = (B + 255) / 256;
+    int nl[kPer];
+    int fx = 0, py = 0;
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int i = threadIdx.x * per + c;
+      nl[c] = 0;
+      if (c < per && i < B) {
+        nl[c] = clamped_len<BS>(a, i);
+        fx += nl[c] / kPartition;
+        py += (nl[c] % kPartition != 0 || nl[c] == 0) ? 1 : 0;
+      }
+    }
+    int ex, ey, tx, ty;
+    block_scan2(sc, fx, py, ex, ey, tx, ty);
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int i = threadIdx.x * per + c;
+      if (c < per && i < B) {
+        sc.full[i] = ex;
+        sc.part[i] = ey;
+        sc.n[i] = nl[c];
+        ex += nl[c] / kPartition;
+        ey += (nl[c] % kPartition != 0 || nl[c] == 0) ? 1 : 0;
+      }
+    }
+    if (threadIdx.x == 0) {
+      sc.full[B] = tx;
+      sc.part[B] = ty;
+      s_next[0] = atomicAdd(&queue[0], 1);
+      s_next[1] = atomicAdd(&queue[0], 1);
+    }
+    __syncthreads();
+  }
+  const int n_full_items = sc.full[B] * a.hkv;
+  const int total = n_full_items + sc.part[B] * a.hkv;
+
+  // Block ids of this wave's steps (0 for steps past the item's end) and the
+  // query slices of one item.
+  struct Plan {
+    QItem it;
+    int idA[kSteps], idB[kSteps];
+  };
+  auto plan_item = [&](int k, Plan& pl, bf16x8 (&qv)[KS]) {
+    const bool live = k < total;
+    if (live) {
+      resolve_item(sc, B, a.hkv, n_full_items, k, pl.it);
+    } else {
+      pl.it = QItem{0, 0, 0, 1, 0, 0, 0};
+    }
+    const int32_t* trow = a.tables + static_cast<int64_t>(pl.it.b) * a.mb;
+#pragma unroll
+    for (int s2 = 0; s2 < kSteps; ++s2) {
+      const int t0 = pl.it.tok0 + kStep * (wave + kWaves * s2);
+      const bool valid = t0 < pl.it.tok1;
+      const int base = t0 / BS;
+      const int ia = trow[min(base, a.mb - 1)];
+      const int ib = (BS == 16) ? trow[min(base + 1, a.mb - 1)] : ia;
+      pl.idA[s2] = valid ? clamp_block(ia, a.nb) : 0;
+      pl.idB[s2] = (valid && (BS == 32 || t0 + 16 < pl.it.tok1)) ? clamp_block(ib, a.nb)
+                                                                 : pl.idA[s2];
+    }
+    // query rows g*G .. g*G+G-1; lanes past the group read a valid row, then zero
+    const uint16_t* qr =
+        q + (static_cast<int64_t>(pl.it.b) * a.hq + pl.it.g * G + min(r, G - 1)) * D + 8 * kg;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const u32x4 w = ld16(qr + 32 * s2);
+      qv[s2] = __builtin_bit_cast(bf16x8, (r < G) ? w : u32x4{0u, 0u, 0u, 0u});
+    }
+  };
+  Eng eng;
+  typename Eng::KV kv[2];
+  auto issue = [&](const Plan& pl, int s2, typename Eng::KV& buf) {
+    const int64_t kofs = static_cast<int64_t>(pl.it.g) * BS * D;
+    const int64_t vofs =
+        static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(pl.it.g) * D * BS;
+    const bool live = pl.it.tok0 + kStep * (wave + kWaves * s2) < pl.it.tok1;
+    eng.load_kv(buf, pool, a.blk_elems, kofs, vofs, pl.idA[s2], pl.idB[s2], lane, live);
+  };
+
+  int cur_k = s_next[0], nxt_k = s_next[1];
+  __syncthreads();  // both slots read before either is rewritten
+  int parity = 0;
+  Plan cur, nxt;
+  bf16x8 qcur[KS], qnxt[KS];
+  plan_item(cur_k, cur, qcur);
+  issue(cur, 0, kv[0]);
+  issue(cur, 1, kv[1]);
+  while (cur_k < total) {
+    plan_item(nxt_k, nxt, qnxt);
+    eng.init();
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) eng.qreg[0][s2] = qcur[s2];
+    if (r < G) eng.lim[0] = cur.it.tok1 - 1;
+    // -- steps of the current item; the next item's first two steps follow ------
+#pragma unroll
+    for (int s2 = 0; s2 < kSteps; ++s2) {
+      const int t0 = cur.it.tok0 + kStep * (wave + kWaves * s2);
+      if (t0 < cur.it.tok1) eng.compute(kv[s2 & 1], t0, cur.it.tok1, lane, a.sl2e);
+      if (s2 == kSteps - 2 && threadIdx.x == 0) {
+        // Take the item after next. The result goes to LDS inside this branch:
+        // only this wave waits for it, at a point where its remaining loads of
+        // the current item are needed next anyway.
+        s_next[parity] = atomicAdd(&queue[0], 1);
+      }
+      if (s2 + 2 < kSteps)
+        issue(cur, s2 + 2, kv[s2 & 1]);
+      else
+        issue(nxt, s2 + 2 - kSteps, kv[s2 & 1]);
+    }
+    // -- merge the waves of the current item, publish --------------------------
+    // One barrier per item: the wave states and the queue slot alternate
+    // between two LDS copies, so item i+2 reuses item i's copy only after
+    // every thread has passed item i+1's barrier, i.e. finished item i.
+    MergeSmem<D>& sm = sm2[parity];
+    const float lt = sum_over_groups(eng.l[0]);
+    if (r < G) {
+      if (kg == 0) {
+        sm.m[wave][r] = eng.m[0];
+        sm.l[wave][r] = lt;
+      }
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j)
+        *reinterpret_cast<f32x4*>(&sm.o[wave][r][16 * j + 4 * kg]) = eng.o[0][j];
+    }
+    __syncthreads();
+    const int after_k = s_next[parity];
+    const int64_t row0 = static_cast<int64_t>(cur.it.b) * a.hq + cur.it.g * G;
+    finish_partition<D, uint16_t>(sm, G, cur.it.np, cur.it.p, a.np_max,
+                                  static_cast<uint16_t*>(a.out) + row0 * D,
+                                  a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2);
+    parity ^= 1;
+    cur = nxt;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) qcur[s2] = qnxt[s2];
+    cur_k = nxt_k;
+    nxt_k = after_k;
+  }
+  if (threadIdx.x == 0) {
+    const int done = atomicAdd(&queue[1], 1);
+    if (done == static_cast<int>(gridDim.x) - 1) {  // everyone else has left
+      atomicExch(&queue[0], 0);
+      atomicExch(&queue[1], 0);
+    }
+  }
 }
 
 template <int D, int BS, int G>
@@ -554,8 +832,42 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
   }
   __syncthreads();
   finish_partition<D, float>(sm, G, it.np, it.p, a.np_max, static_cast<float*>(a.out) + row0 * D,
-                             a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2,
-                             a.ws_cnt + (static_cast<int64_t>(it.b) * a.hkv + it.g));
+                             a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2);
+}
+
+// Split-K merge: one workgroup per (sequence, kv head) with more than one
+// partition combines the partitions' (M, L, O) by the log-sum-exp identity
+// M* = max M_j, L* = sum L_j 2^(M_j - M*), o = sum O_j 2^(M_j - M*) / L*.
+template <int D, int BS, typename OutT>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  const int bg = blockIdx.x;
+  if (bg >= a.num_seqs * a.hkv) return;
+  const int b = bg / a.hkv, g = bg - b * a.hkv;
+  int n = a.lens[b];
+  n = n < 0 ? 0 : n;
+  n = n > a.max_ctx ? a.max_ctx : n;
+  n = n > a.mb * BS ? a.mb * BS : n;
+  const int np = (n + kPartition - 1) / kPartition;
+  if (np <= 1) return;
+  const int G = a.hq / a.hkv;
+  const int64_t row0 = static_cast<int64_t>(b) * a.hq + g * G;
+  OutT* out = static_cast<OutT*>(a.out) + row0 * D;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int row = idx / D, dd = idx - row * D;
+    const float* mlr = a.ws_ml + (row0 + row) * a.np_max * 2;
+    const float* orow = a.ws_o + (row0 + row) * a.np_max * D + dd;
+    float M = -__builtin_inff();
+    for (int pp = 0; pp < np; ++pp) M = fmaxf(M, mlr[2 * pp]);
+    float L = 0.f, O = 0.f;
+    if (M != -__builtin_inff()) {
+      for (int pp = 0; pp < np; ++pp) {
+        const float f = exp2_fast(mlr[2 * pp] - M);
+        L = fmaf(mlr[2 * pp + 1], f, L);
+        O = fmaf(orow[static_cast<int64_t>(pp) * D], f, O);
+      }
+    }
+    store_out<OutT>(out + idx, L > 0.f ? O / L : 0.f);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -683,7 +995,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
   }
   __syncthreads();
   finish_partition<D, float>(sm, G, 1, 0, 1, static_cast<float*>(a.out) + row0 * D, nullptr,
-                             nullptr, nullptr);
+                             nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -752,9 +1064,31 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Dispatch helpers.
 // ---------------------------------------------------------------------------
+// Workgroups that fit on the device at once for `kernel` (0 if unknown).
+template <typename K>
+int resident_workgroups(K kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+
 template <int D, int BS>
-hipError_t launch_decode_bf16(const DecodeArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_bf16_kernel<D, BS>), dim3(grid), dim3(256), 0, st, a);
+hipError_t launch_decode_bf16(const DecodeArgs& a, int grid, int32_t* queue, hipStream_t st) {
+  if (a.num_seqs <= kMaxScanSeqs) {
+    static const int resident = resident_workgroups(decode_bf16_persistent_kernel<D, BS>);
+    const int w = min(grid, resident > 0 ? resident : 512);
+    hipLaunchKernelGGL((decode_bf16_persistent_kernel<D, BS>), dim3(w), dim3(256), 0, st, a,
+                       queue);
+  } else {
+    hipLaunchKernelGGL((decode_bf16_kernel<D, BS>), dim3(grid), dim3(256), 0, st, a);
+  }
+  if (a.np_max > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<D, BS, uint16_t>), dim3(a.num_seqs * a.hkv), dim3(256),
+                       0, st, a);
   return hipGetLastError();
 }
 
@@ -767,6 +1101,9 @@ hipError_t launch_decode_f32(const DecodeArgs& a, int G, int grid, hipStream_t s
     case 8: hipLaunchKernelGGL((decode_f32_kernel<D, BS, 8>), dim3(grid), dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
+  if (a.np_max > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<D, BS, float>), dim3(a.num_seqs * a.hkv), dim3(256), 0,
+                       st, a);
   return hipGetLastError();
 }
 
@@ -856,17 +1193,17 @@ hipError_t launch_decode(void* out, const void* q, const void* pool, const int32
   a.sl2e = scale * kLog2e;
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
-  a.ws_cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.cnt_off);
+  int32_t* queue = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.queue_off);
   const int64_t items = static_cast<int64_t>(num_seqs) * ps.num_kv_heads * np_max;
   a.n_items = static_cast<int>(items);
-  const int grid = static_cast<int>((items + 7) / 8 * 8);
+  const int grid = static_cast<int>(items);
   const int G = num_q_heads / ps.num_kv_heads;
   const int D = ps.head_dim, BS = ps.block_size;
   if (dtype == 1) {
-    if (D == 64 && BS == 16) return launch_decode_bf16<64, 16>(a, grid, st);
-    if (D == 64 && BS == 32) return launch_decode_bf16<64, 32>(a, grid, st);
-    if (D == 128 && BS == 16) return launch_decode_bf16<128, 16>(a, grid, st);
-    if (D == 128 && BS == 32) return launch_decode_bf16<128, 32>(a, grid, st);
+    if (D == 64 && BS == 16) return launch_decode_bf16<64, 16>(a, grid, queue, st);
+    if (D == 64 && BS == 32) return launch_decode_bf16<64, 32>(a, grid, queue, st);
+    if (D == 128 && BS == 16) return launch_decode_bf16<128, 16>(a, grid, queue, st);
+    if (D == 128 && BS == 32) return launch_decode_bf16<128, 32>(a, grid, queue, st);
   } else {
     if (D == 64 && BS == 16) return launch_decode_f32<64, 16>(a, G, grid, st);
     if (D == 64 && BS == 32) return launch_decode_f32<64, 32>(a, G, grid, st);

@@ -21,20 +21,23 @@ struct PoolShape {
   int64_t block_elems() const { return 2LL * num_kv_heads * block_size * head_dim; }
 };
 
-// Workspace carve-up for pa_decode (all offsets 256-byte aligned).
+// Workspace carve-up for pa_decode (256-byte aligned): the work-queue counters
+// at offset 0 (a place that does not depend on the batch shape), then per
+// (sequence, query head, partition) the partition's unnormalised output O[d]
+// and its (M, L). The counters must be zero before the first call; every call
+// returns them to zero. Partial results need no initialisation.
 struct DecodeWorkspace {
-  size_t o_off, ml_off, cnt_off, total;
+  size_t queue_off, o_off, ml_off, total;
   static DecodeWorkspace layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
                                 int64_t max_parts) {
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
     DecodeWorkspace w;
-    w.o_off = 0;
+    w.queue_off = 0;
+    w.o_off = 256;
     size_t o_bytes = size_t(num_seqs) * num_q_heads * max_parts * head_dim * sizeof(float);
-    w.ml_off = up(o_bytes);
+    w.ml_off = w.o_off + up(o_bytes);
     size_t ml_bytes = size_t(num_seqs) * num_q_heads * max_parts * 2 * sizeof(float);
-    w.cnt_off = w.ml_off + up(ml_bytes);
-    size_t cnt_bytes = size_t(num_seqs) * num_q_heads * sizeof(int32_t);
-    w.total = w.cnt_off + up(cnt_bytes);
+    w.total = w.ml_off + up(ml_bytes);
     return w;
   }
 };

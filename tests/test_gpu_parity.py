@@ -251,8 +251,7 @@ def test_empty_batch_is_a_no_op():
 
 
 def test_repeated_calls_reuse_workspace_and_are_deterministic():
-    """Bit-identical reruns; the workspace's split-K counters return to zero, so a
-    different batch can reuse it."""
+    """Bit-identical reruns, and one workspace serving batches of different shapes."""
     import paged_kv_cache_282_amd as pa
     a = make_workload("gqa", **SMALL["gqa"])
     b = make_workload("mha", num_seqs=10, min_len=600, max_len=3000, num_heads=4)
@@ -298,7 +297,7 @@ def test_high_block_ids_use_64bit_offsets():
     _say(f"[case] 64-bit offsets: pool of {nb_big} blocks = {nb_big * be * 2 / 2**30:.2f} GiB")
     st = DeviceStep(w)
     big = torch.full((nb_big * be,), float("nan"), dtype=torch.bfloat16, device="cuda")
-    big[base * be:] = st.pool
+    big[base * be:] = st.pool.reshape(-1)
     st.pool = big
     st.tables = i32(w.block_tables + base)
     st.slots = i32(w.slot_mapping.astype(np.int64) + base * w.block_size)
