@@ -34,15 +34,19 @@
  * are float32; bfloat16 outputs are rounded to nearest even.
  *
  * KV pool layout (one layer). The pool is `num_blocks` blocks of
- * `2 * num_kv_heads * block_size * head_dim` elements each. Block j holds
- *   K half: [num_kv_heads][block_size][head_dim]  (a token's vector contiguous)
- *   V half: [num_kv_heads][head_dim][block_size]  (a dimension's block_size
- *                                                  token values contiguous)
- * K element (block j, kv head g, slot s, dim i) is at
- *   j*E + (g*block_size + s)*head_dim + i,                     E = 2*Hkv*bs*d;
- * V element (j, g, s, i) is at
- *   j*E + Hkv*bs*d + (g*head_dim + i)*block_size + s.
- * Logical token t of a sequence with table row T lives in block T[t / bs] at
+ * `2 * num_kv_heads * block_size * head_dim` elements each. Block j holds its
+ * K half, then its V half; each half is `num_kv_heads` tiles of
+ * `block_size * head_dim` elements, one per kv head:
+ *   K tile: [head_dim/8][block_size][8]  (8-element slices of each token's
+ *                                         vector; slice c of all slots is
+ *                                         contiguous)
+ *   V tile: [block_size/4][head_dim][4]  (4-token slices of each dimension)
+ * With E = 2*Hkv*bs*d and T = bs*d, K element (block j, kv head g, slot s,
+ * dim i) is at
+ *   j*E + g*T + ((i/8)*bs + s)*8 + i%8,
+ * and V element (j, g, s, i) at
+ *   j*E + Hkv*T + g*T + ((s/4)*d + i)*4 + s%4.
+ * Logical token t of a sequence with table row R lives in block R[t / bs] at
  * slot t % bs. A slot number is `block * block_size + offset`.
  *
  * Supported shapes: head_dim in {64, 128}; block_size in {16, 32};

@@ -2,8 +2,9 @@
 
 Independent of ``oracle.paged_attention``: it reads the pool as a flat list
 with its own index arithmetic (K element (blk, head, slot, dim) at
-``blk*E + (head*bs + slot)*d + dim``; V element at
-``blk*E + Hkv*bs*d + (head*d + dim)*bs + slot`` with ``E = 2*Hkv*bs*d``),
+``blk*E + head*bs*d + ((dim // 8)*bs + slot)*8 + dim % 8``; V element at
+``blk*E + Hkv*bs*d + head*bs*d + ((slot // 4)*d + dim)*4 + slot % 4`` with
+``E = 2*Hkv*bs*d``),
 decodes bfloat16 through ``struct``, and uses explicit loops, ``math.exp`` and
 ``math.fsum``. Only for tiny inputs.
 """
@@ -20,11 +21,12 @@ def _value(word, dtype):
 
 
 def _k_index(blk, head, slot, dim, Hkv, bs, d):
-    return blk * (2 * Hkv * bs * d) + (head * bs + slot) * d + dim
+    return blk * (2 * Hkv * bs * d) + head * bs * d + ((dim // 8) * bs + slot) * 8 + dim % 8
 
 
 def _v_index(blk, head, slot, dim, Hkv, bs, d):
-    return blk * (2 * Hkv * bs * d) + Hkv * bs * d + (head * d + dim) * bs + slot
+    return (blk * (2 * Hkv * bs * d) + Hkv * bs * d + head * bs * d
+            + ((slot // 4) * d + dim) * 4 + slot % 4)
 
 
 def _attend_one(qv, keys, vals, sigma):

@@ -3,9 +3,12 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Pool format (the library's documented layout): ``pool`` is ``[num_blocks,
-2*Hkv*bs*d]`` storage elements. Block ``j`` holds its K half ``[Hkv][bs][d]``
-then its V half ``[Hkv][d][bs]``. Elements are float32 values or bfloat16 bit
-patterns (uint16); both decode exactly to float64.
+2*Hkv*bs*d]`` storage elements. Block ``j`` holds its K half then its V half.
+Per kv head, the K half is ``[d/8][bs][8]`` (dimension i of slot s at
+``((i // 8) * bs + s) * 8 + i % 8``) and the V half is ``[bs/4][d][4]``
+(dimension i of slot s at ``((s // 4) * d + i) * 4 + s % 4``). Elements are
+float32 values or bfloat16 bit patterns (uint16); both decode exactly to
+float64.
 """
 from __future__ import annotations
 
@@ -29,11 +32,11 @@ def decode_elements(raw: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def pool_views(pool: np.ndarray, num_kv_heads: int, block_size: int, head_dim: int):
-    """Views of the raw pool: K as [blk][head][slot][dim], V as [blk][head][dim][slot]."""
+    """Views of the raw pool: K as [blk][head][d/8][slot][8], V as [blk][head][slot/4][d][4]."""
     nb = pool.shape[0]
     halves = pool.reshape(nb, 2, num_kv_heads * block_size * head_dim)
-    k = halves[:, 0].reshape(nb, num_kv_heads, block_size, head_dim)
-    v = halves[:, 1].reshape(nb, num_kv_heads, head_dim, block_size)
+    k = halves[:, 0].reshape(nb, num_kv_heads, head_dim // 8, block_size, 8)
+    v = halves[:, 1].reshape(nb, num_kv_heads, block_size // 4, head_dim, 4)
     return k, v
 
 
@@ -51,8 +54,8 @@ def gather(pool, dtype, table_row, n, g, num_kv_heads, block_size, head_dim):
     t = np.arange(n)
     blk = np.asarray(table_row)[t // block_size]
     off = t % block_size
-    k = kview[blk, g, off, :]          # [n][d]
-    v = vview[blk, g, :, off]          # [n][d] (advanced indices first)
+    k = kview[blk, g, :, off, :].reshape(n, head_dim)     # [n][d/8][8] -> [n][d]
+    v = vview[blk, g, off // 4, :, off % 4]                # [n][d]
     return decode_elements(k, dtype), decode_elements(v, dtype)
 
 
@@ -141,8 +144,8 @@ def append(pool, k_new, v_new, slot_mapping, num_kv_heads, block_size, head_dim)
         if s < 0:
             continue
         blk, off = divmod(int(s), block_size)
-        kview[blk, :, off, :] = k_new[i]
-        vview[blk, :, :, off] = v_new[i]
+        kview[blk, :, :, off, :] = k_new[i].reshape(num_kv_heads, head_dim // 8, 8)
+        vview[blk, :, off // 4, :, off % 4] = v_new[i]
     return out
 
 

@@ -17,10 +17,11 @@
 //     sequence merges the partitions (log-sum-exp identity) and writes out.
 //   * bf16: scores and p.V run on v_mfma_f32_16x16x32_bf16. The 16 columns of
 //     each MFMA are the query heads of one GQA group (padded) or, in prefill,
-//     (position, head) rows. K tokens are assigned to MFMA rows so that each
-//     lane's eight scores are exactly the eight tokens whose V^T values the
-//     same lane loads as one 16-byte operand for p.V: probabilities never
-//     leave registers. V is stored dimension-major in the pool for this.
+//     (position, head) rows. The pool keeps K in 8-element slices and V in
+//     4-token slices, so every MFMA operand is one contiguous load and each
+//     lane's eight scores are exactly the eight tokens whose V values the same
+//     lane holds for p.V: probabilities never leave registers. Every load
+//     instruction reads a single block through a uniform base address.
 //   * Tokens outside a context are excluded by selection (-inf scores, zeroed
 //     V), never by multiplying with p = 0, so NaN in unused slots is harmless.
 //   * fp32: a VALU kernel with the same work decomposition (16 lanes per token
@@ -36,6 +37,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ constexpr bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -53,9 +57,17 @@ __device__ __forceinline__ f32x4 ld16f(const float* p) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
+// Maximum over the four 16-lane rows of the wave at each lane position: swap
+// halves, then neighbouring rows, with the cross-lane VALU permutes.
 __device__ __forceinline__ float max_over_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  // (vector elements are read by value: bit casts of an element expression
+  // have read element 0)
+  const uint32_t u = __float_as_uint(x);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 __device__ __forceinline__ float sum_over_groups(float x) {
   x += __shfl_xor(x, 16);
@@ -90,16 +102,18 @@ __device__ __forceinline__ int clamp_block(int blk, int64_t nb) {
 // bf16 MFMA engine: online-softmax attention of NT column tiles of 16 query
 // rows over 32-token steps of one kv head.
 //
+// A step is 32 tokens: set a = tokens 0..15, set b = tokens 16..31 (two
+// blocks of 16, or the two halves of one block of 32).
 // Lane (kg = lane/16, r = lane%16):
 //   score MFMA  S^T[tok][row] = K[tok][:] . Q[row][:]
-//     A (K)  lane gives K[T(r)][32s + 8kg .. +7]   (set a: T = 8(r/4) + r%4,
-//                                                  set b: T + 4)
+//     A (K)  lane gives slice 4s+kg of token r of the set (16 contiguous bytes;
+//            a quarter-wave reads 256 contiguous bytes)
 //     B (Q)  lane gives Q[row r][32s + 8kg .. +7]
-//     C      lane (kg, n) gets tokens 8kg+i (set a) and 8kg+4+i (set b), i<4,
-//            of row n: the eight tokens 8kg .. 8kg+7.
+//     C      lane (kg, n) gets tokens 4kg+i of set a and of set b, i < 4.
 //   p.V MFMA   O^T[dim][row] += V^T[dim][tok] . P^T[tok][row]
-//     A (V^T) lane gives V^T[16j + r][tok 8kg .. +7]  (16 contiguous bytes)
-//     B (P)   lane gives P[row n][tok 8kg .. +7]      (its own eight scores)
+//     A (V^T) lane gives dim 16j + r at tokens 4kg..4kg+3 of set a and of set
+//             b: two 8-byte 4-token slices
+//     B (P)   lane gives row n at the same eight tokens (its own scores)
 //     C       lane (kg, n) holds O^T[16j + 4kg + i][n], i < 4.
 // ---------------------------------------------------------------------------
 template <int D, int BS, int NT>
@@ -143,58 +157,57 @@ struct Bf16Engine {
                                           int64_t blk_elems, int64_t kofs, int64_t vofs, int blkA,
                                           int blkB, int lane, bool live = true) const {
     // A step that will not be computed (live == false) still issues its loads,
-    // so that the number of loads in flight is the same on every path, but
-    // every lane reads the same 16 bytes: one cache line per instruction.
+    // so that the number of loads in flight is the same on every path, but it
+    // reads block 0 and every lane of an instruction reads the same 16 bytes.
+    // The block bases are wave-uniform (scalar registers); each load adds the
+    // lane's constant offset and a compile-time displacement.
     const int r = lane & 15, kg = lane >> 4;
-    const uint16_t* baseA = pool + static_cast<int64_t>(blkA) * blk_elems;
-    const uint16_t* baseB = pool + static_cast<int64_t>(blkB) * blk_elems;
-    const int ta = ((r >> 2) << 3) | (r & 3);
-    const int tb = ta + 4;
-    const uint16_t* ka;
-    const uint16_t* kb;
-    if constexpr (BS == 16) {
-      ka = (ta < 16 ? baseA : baseB) + kofs + (ta & 15) * D + 8 * kg;
-      kb = (tb < 16 ? baseA : baseB) + kofs + (tb & 15) * D + 8 * kg;
-    } else {
-      ka = baseA + kofs + ta * D + 8 * kg;
-      kb = baseA + kofs + tb * D + 8 * kg;
-    }
-    const uint16_t* vp;
-    if constexpr (BS == 16)
-      vp = (kg < 2 ? baseA : baseB) + vofs + 8 * (kg & 1);
-    else
-      vp = baseA + vofs + 8 * kg;
-    const int ks = live ? 32 : 0;
-    const int vs = live ? BS : 0;
-    if (!live) {
-      ka = pool;
-      kb = pool;
-      vp = pool;
-    }
+    if (!live) blkA = blkB = 0;
+    blkA = __builtin_amdgcn_readfirstlane(blkA);
+    blkB = __builtin_amdgcn_readfirstlane(blkB);
+    const uint16_t* bA = pool + static_cast<int64_t>(blkA) * blk_elems;
+    const uint16_t* bB = (BS == 16) ? pool + static_cast<int64_t>(blkB) * blk_elems : bA;
+    const uint16_t* kta = bA + kofs;                                 // set a, slice 0
+    const uint16_t* ktb = bB + kofs + (BS == 16 ? 0 : 16 * 8);       // set b, slice 0
+    const uint16_t* vta = bA + vofs;                                 // set a, 4-token slice 0
+    const uint16_t* vtb = bB + vofs + (BS == 16 ? 0 : 4 * D * 4);    // set b, 4-token slice 0
+    // lane's K element offset (slice kg, token r) and V offset (4-token slice
+    // kg, dim r)
+    const uint32_t ko = live ? static_cast<uint32_t>((kg * BS + r) * 8) : 0u;
+    const uint32_t vo = live ? static_cast<uint32_t>((kg * D + r) * 4) : 0u;
+    constexpr int ks = 4 * BS * 8;  // next 4 slices of K
+    constexpr int vs = 16 * 4;      // next 16 dims of V
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kv.kA[s] = ld16(ka + ks * s);
-      kv.kB[s] = ld16(kb + ks * s);
+      kv.kA[s] = ld16(kta + ko + ks * s);
+      kv.kB[s] = ld16(ktb + ko + ks * s);
     }
 #pragma unroll
-    for (int j = 0; j < VT; ++j) kv.vv[j] = ld16(vp + (16 * j + r) * vs);
+    for (int j = 0; j < VT; ++j) {
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(vta + vo + vs * j);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(vtb + vo + vs * j);
+      kv.vv[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
   }
 
   // Consume a loaded step starting at token t0. Tokens >= vend have their V
   // zeroed (they may be NaN); scores of tokens past a row's limit are -inf.
   __device__ __forceinline__ void compute(KV& kv, int t0, int vend, int lane, float sl2e) {
     const int kg = lane >> 4;
+    // element e of this lane's eight tokens: e < 4 -> t0 + 4kg + e (set a),
+    // e >= 4 -> t0 + 16 + 4kg + e - 4 (set b)
+    const int ta0 = t0 + 4 * kg, tb0 = t0 + 16 + 4 * kg;
     if (t0 + 32 > vend) {  // wave-uniform: zero V of tokens past the end
-      const int nvalid = vend - t0 - 8 * kg;
+      const int na = vend - ta0, nb = vend - tb0;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t mask = (2 * w < nvalid ? 0x0000FFFFu : 0u) |
-                              (2 * w + 1 < nvalid ? 0xFFFF0000u : 0u);
+        const int nv = w < 2 ? na : nb;
+        const int e0 = 2 * (w & 1);
+        const uint32_t mask = (e0 < nv ? 0x0000FFFFu : 0u) | (e0 + 1 < nv ? 0xFFFF0000u : 0u);
 #pragma unroll
         for (int j = 0; j < VT; ++j) kv.vv[j][w] &= mask;
       }
     }
-    const int tbase = t0 + 8 * kg;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -205,38 +218,53 @@ struct Bf16Engine {
         sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv.kB[s]),
                                                      qreg[nt][s], sb, 0, 0, 0);
       }
+      // raw scores q.k; the softmax runs in base 2 on q.k * sl2e
       float sc[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sc[i] = sa[i] * sl2e;
-        sc[4 + i] = sb[i] * sl2e;
+        sc[i] = sa[i];
+        sc[4 + i] = sb[i];
       }
-      float mx = -__builtin_inff();
+      // Mask the scores of tokens past a row's limit. Only steps that reach
+      // past the limit of some real row need it (wave-uniform test); then
+      // padding rows (lim < 0) are masked entirely, otherwise their scores are
+      // finite and are never read.
+      if (__builtin_amdgcn_ballot_w64(lim[nt] >= 0 && t0 + 31 > lim[nt]) != 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sc[e] = (tbase + e <= lim[nt]) ? sc[e] : -__builtin_inff();
-        mx = fmaxf(mx, sc[e]);
+        for (int e = 0; e < 8; ++e) {
+          const int tok = e < 4 ? ta0 + e : tb0 + e - 4;
+          sc[e] = (tok <= lim[nt]) ? sc[e] : -__builtin_inff();
+        }
       }
+      float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
       mx = max_over_groups(mx);
-      const float mnew = fmaxf(m[nt], mx);
+      // scaling by sl2e > 0 is monotone, so the scaled maximum is mx * sl2e
+      const float mnew = fmaxf(m[nt], mx * sl2e);
       const float muse = (mnew == -__builtin_inff()) ? 0.f : mnew;
       const float alpha = exp2_fast(m[nt] - muse);
       bf16x8 p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = static_cast<__bf16>(exp2_fast(fmaf(sc[e], sl2e, -muse)));
+      // the row sum adds the bf16 weights that p.V uses
       float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 pb = static_cast<__bf16>(exp2_fast(sc[e] - muse));
-        p[e] = pb;
-        ps += static_cast<float>(pb);
-      }
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), kOnes2, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), kOnes2, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), kOnes2, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), kOnes2, ps, false);
       l[nt] = l[nt] * alpha + ps;
+      // o needs rescaling only where a finite maximum grew (elsewhere alpha is
+      // 1, or o is still zero)
+      const bool grew = m[nt] != -__builtin_inff() && mnew > m[nt];
       m[nt] = mnew;
+      if (__builtin_amdgcn_ballot_w64(grew) != 0) {
 #pragma unroll
-      for (int j = 0; j < VT; ++j) {
-        o[nt][j] *= alpha;
+        for (int j = 0; j < VT; ++j) o[nt][j] *= alpha;
+      }
+#pragma unroll
+      for (int j = 0; j < VT; ++j)
         o[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv.vv[j]),
                                                            p, o[nt][j], 0, 0, 0);
-      }
     }
   }
 
@@ -253,8 +281,8 @@ struct Bf16Engine {
 // fp32 VALU engine: G query rows (one GQA group) of one kv head.
 // Lane (grp = lane/16, c = lane%16). In a 32-token step, group grp owns tokens
 // 8grp .. 8grp+7. q.K: lane holds dims c*EPL .. +EPL of a K row; the 16 lanes
-// sum their partial dot products. p.V: lane owns dims c + 16k and reads 8
-// consecutive tokens of each from the dimension-major V half.
+// sum their partial dot products. p.V: lane owns dims c + 16k and reads the
+// two 4-token V slices of those 8 tokens.
 // ---------------------------------------------------------------------------
 template <int D, int BS, int G>
 struct F32Engine {
@@ -293,9 +321,11 @@ struct F32Engine {
     }
     const int tbase = t0 + 8 * grp;
     float s[8][G];
+    // lane's K dims c*EPL .. +EPL lie in one 8-element slice
+    const int kslice = (c * EPL) / 8, ksub = (c * EPL) % 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float* kr = base + kofs + (slot0 + e) * D + c * EPL;
+      const float* kr = base + kofs + (kslice * BS + slot0 + e) * 8 + ksub;
       float kv[EPL];
 #pragma unroll
       for (int k4 = 0; k4 < EPL / 4; ++k4) {
@@ -336,9 +366,10 @@ struct F32Engine {
     const bool tail = t0 + 32 > vend;
 #pragma unroll
     for (int k = 0; k < EPL; ++k) {
-      const float* vr = base + vofs + (c + 16 * k) * BS + slot0;
+      // dim c + 16k at tokens slot0 .. slot0+7: two 4-token slices
+      const float* vr = base + vofs + ((slot0 / 4) * D + c + 16 * k) * 4;
       float v[8];
-      const f32x4 w0 = ld16f(vr), w1 = ld16f(vr + 4);
+      const f32x4 w0 = ld16f(vr), w1 = ld16f(vr + D * 4);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         v[x] = w0[x];
@@ -614,6 +645,18 @@ __device__ __forceinline__ void resolve_item(const ScanSmem& sc, int B, int hkv,
   it.nsteps = (it.tok1 - it.tok0 + kStep - 1) / kStep;
 }
 
+// An item is the same for the whole workgroup; say so, so that everything
+// derived from it lives in scalar registers.
+__device__ __forceinline__ void make_uniform(QItem& it) {
+  it.b = __builtin_amdgcn_readfirstlane(it.b);
+  it.g = __builtin_amdgcn_readfirstlane(it.g);
+  it.p = __builtin_amdgcn_readfirstlane(it.p);
+  it.np = __builtin_amdgcn_readfirstlane(it.np);
+  it.tok0 = __builtin_amdgcn_readfirstlane(it.tok0);
+  it.tok1 = __builtin_amdgcn_readfirstlane(it.tok1);
+  it.nsteps = __builtin_amdgcn_readfirstlane(it.nsteps);
+}
+
 // Items are processed as a pipeline. The queue runs two items ahead: while
 // item i computes, every wave already holds the block ids and query of item
 // i+1, and as soon as a wave finishes its steps of item i it issues the first
@@ -696,6 +739,7 @@ void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
     } else {
       pl.it = QItem{0, 0, 0, 1, 0, 0, 0};
     }
+    make_uniform(pl.it);
     const int32_t* trow = a.tables + static_cast<int64_t>(pl.it.b) * a.mb;
 #pragma unroll
     for (int s2 = 0; s2 < kSteps; ++s2) {
@@ -1001,8 +1045,9 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 // KV append and block copy (pure data movement).
 // ---------------------------------------------------------------------------
-// Thread -> (token, kv head, 8-element chunk). K: one contiguous 8-element run;
-// V: 8 elements spaced block_size apart in the dimension-major V half.
+// Thread -> (token, kv head, 8-element slice). K: the slice is one contiguous
+// 8-element run; V: its 8 dimensions sit 4 elements apart in the token's
+// 4-token slice.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void append_kernel(T* __restrict__ pool,
                                                      const T* __restrict__ kn,
@@ -1022,9 +1067,11 @@ __global__ __launch_bounds__(256) void append_kernel(T* __restrict__ pool,
   const int64_t blk = slot / bs;
   const int off = slot - static_cast<int>(blk) * bs;
   const int64_t src = (tok * hkv + h) * D + ch * 8;
-  T* kd = pool + blk * blk_elems + (static_cast<int64_t>(h) * bs + off) * D + ch * 8;
-  T* vd = pool + blk * blk_elems + static_cast<int64_t>(hkv) * bs * D +
-          (static_cast<int64_t>(h) * D + ch * 8) * bs + off;
+  const int64_t tile = static_cast<int64_t>(h) * bs * D;
+  // K: slice ch of slot off; V: dims ch*8 .. +7 of slot off, 4 elements apart
+  T* kd = pool + blk * blk_elems + tile + (static_cast<int64_t>(ch) * bs + off) * 8;
+  T* vd = pool + blk * blk_elems + static_cast<int64_t>(hkv) * bs * D + tile +
+          (static_cast<int64_t>(off / 4) * D + ch * 8) * 4 + off % 4;
   constexpr int W = 8 * sizeof(T) / 16;  // 16-byte words per chunk
 #pragma unroll
   for (int w = 0; w < W; ++w) st16(kd + w * (16 / sizeof(T)), ld16(kn + src + w * (16 / sizeof(T))));
@@ -1035,7 +1082,7 @@ __global__ __launch_bounds__(256) void append_kernel(T* __restrict__ pool,
     *reinterpret_cast<u32x4*>(&v[w * (16 / sizeof(T))]) = x;
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) vd[static_cast<int64_t>(e) * bs] = v[e];
+  for (int e = 0; e < 8; ++e) vd[4 * e] = v[e];
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ pool,

@@ -1,7 +1,8 @@
 """Test-side writer of the pool layout, independent of the oracle and the library.
 
 Writes logical tokens of contiguous per-sequence K/V into a pool of the
-documented layout: block j = K half [Hkv][bs][d] then V half [Hkv][d][bs].
+documented layout: block j = K half [Hkv][d/8][bs][8] then V half
+[Hkv][bs/4][d][4].
 """
 from __future__ import annotations
 
@@ -16,8 +17,9 @@ def put_token(pool, blk, slot, k_heads, v_heads, Hkv, bs, d):
     """k_heads, v_heads: [Hkv][d] values of one token."""
     for g in range(Hkv):
         for i in range(d):
-            pool[blk, g * bs * d + slot * d + i] = k_heads[g][i]
-            pool[blk, Hkv * bs * d + g * d * bs + i * bs + slot] = v_heads[g][i]
+            pool[blk, g * bs * d + ((i // 8) * bs + slot) * 8 + i % 8] = k_heads[g][i]
+            pool[blk, Hkv * bs * d + g * bs * d + ((slot // 4) * d + i) * 4 + slot % 4] = \
+                v_heads[g][i]
 
 
 def contiguous_pool(K, V, bs, dtype=np.float32):

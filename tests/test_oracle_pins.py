@@ -50,14 +50,15 @@ def test_golden_hand_worked(case):
         for t, (blk, slot) in enumerate(seq["placement"]):
             # placement must be what the table implies for logical token t
             assert seq["table"][t // bs] == blk and t % bs == slot
-            kk = [[np.nan if x is None else x for x in h] for h in seq["k"][t]]
-            vv = [[np.nan if x is None else x for x in h] for h in seq["v"][t]]
+            pad = lambda h: [np.nan if x is None else x for x in h] + [0.0] * (d - len(h))  # noqa: E731
+            kk = [pad(h) for h in seq["k"][t]]
+            vv = [pad(h) for h in seq["v"][t]]
             put_token(pool, blk, slot, kk, vv, Hkv, bs, d)
         tables.append(seq["table"])
         lens.append(len(seq["placement"]))
     width = max(len(t) for t in tables)
     tab = np.array([t + [0] * (width - len(t)) for t in tables], np.int32)
-    q = np.array(case["q"], np.float32)
+    q = np.array([[h + [0.0] * (d - len(h)) for h in row] for row in case["q"]], np.float32)
     if case["kind"] == "decode":
         out = oracle.decode(q, pool, tab, np.array(lens), Hkv, bs, case["scale"], "f32")
     else:
@@ -98,8 +99,9 @@ def test_append_bitwise_against_brute(name):
     touched = np.zeros(w.pool.shape, bool)
     kv, vv = oracle.pool_views(touched, w.num_kv_heads, w.block_size, w.head_dim)
     for s in w.slot_mapping:
-        kv[s // w.block_size, :, s % w.block_size, :] = True
-        vv[s // w.block_size, :, :, s % w.block_size] = True
+        off = s % w.block_size
+        kv[s // w.block_size, :, :, off, :] = True
+        vv[s // w.block_size, :, off // 4, :, off % 4] = True
     assert np.array_equal(a.view(view)[~touched], w.pool.view(view)[~touched])
     assert touched.sum() == len(w.slot_mapping) * 2 * w.num_kv_heads * w.head_dim
 
@@ -337,8 +339,8 @@ def test_merge_of_all_empty_parts_is_zero():
 def test_decode_matches_brute_force_on_tiny_random(seed):
     rng = np.random.default_rng(100 + seed)
     B = int(rng.integers(1, 5))
-    bs = int(rng.choice([1, 2, 16]))
-    d = int(rng.choice([1, 4, 8]))
+    bs = int(rng.choice([4, 8, 16]))
+    d = int(rng.choice([8, 16]))
     Hkv = int(rng.choice([1, 2]))
     G = int(rng.choice([1, 2]))
     lens = rng.integers(1, 41, size=B)
@@ -364,13 +366,13 @@ def test_decode_matches_brute_force_on_tiny_config():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_prefill_matches_brute_force(dtype):
     w = make_workload("mixed", num_decode=2, dec_min=3, dec_max=20, num_chunks=3, chunk_len=5,
-                      max_prior=11, num_q_heads=4, num_kv_heads=2, head_dim=4, block_size=2,
+                      max_prior=11, num_q_heads=4, num_kv_heads=2, head_dim=8, block_size=4,
                       dtype=dtype)
     a = _appended(w)
     o = oracle.prefill(w.prefill_q, a, w.prefill_block_tables, w.prefill_context_lens,
-                       w.query_start_loc, 2, 2, w.scale, dtype)
+                       w.query_start_loc, 2, 4, w.scale, dtype)
     ob = np.array(brute.prefill(w.prefill_q, a, w.prefill_block_tables, w.prefill_context_lens,
-                                w.query_start_loc, 2, 2, w.scale, dtype))
+                                w.query_start_loc, 2, 4, w.scale, dtype))
     assert np.abs(o - ob).max() <= 1e-12
     assert not np.isnan(o).any()
 

@@ -64,9 +64,9 @@ def test_unused_slots_are_poison():
         if j not in used:
             assert (w.pool[j] == nan).all()
     # the appended token's slot is poison before the append
-    kview = w.pool.reshape(w.num_blocks, 2, 2, w.block_size, 8)[:, 0]
+    kview = w.pool.reshape(w.num_blocks, 2, 2, 1, w.block_size, 8)[:, 0]  # d = 8: one slice
     for s in w.slot_mapping:
-        assert (kview[s // w.block_size, :, s % w.block_size] == nan).all()
+        assert (kview[s // w.block_size, :, :, s % w.block_size] == nan).all()
 
 
 def test_prefix_config_shares_and_copies():

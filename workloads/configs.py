@@ -10,9 +10,9 @@ worth, measured": output lengths of high variance, up to 1536 tokens).
 
 Storage format written here (the library's documented pool layout): the pool is
 ``num_blocks`` blocks; block ``j`` holds ``2 * Hkv * bs * d`` elements, first the
-K half laid out ``[Hkv][bs][d]`` (one token's head vector contiguous), then the
-V half laid out ``[Hkv][d][bs]`` (one dimension's ``bs`` token values
-contiguous). Block ``num_blocks - 1`` is a poison block filled with NaN; every
+K half laid out ``[Hkv][d/8][bs][8]`` (8-element slices of a token's vector),
+then the V half laid out ``[Hkv][bs/4][d][4]`` (4-token slices of each
+dimension). Block ``num_blocks - 1`` is a poison block filled with NaN; every
 table entry past a sequence's last block points at it, and every slot that
 holds no cached token is NaN too, so a read outside a context is visible.
 
@@ -98,11 +98,13 @@ def _make_pool(ss, nb_total: int, hkv: int, bs: int, d: int, dtype: str,
     per_block = 2 * hkv * bs * d
     pool = normal_values(ss, nb_total * per_block, dtype).reshape(nb_total, per_block)
     halves = pool.reshape(nb_total, 2, hkv * bs * d)
-    k_view = halves[:, 0].reshape(nb_total, hkv, bs, d).transpose(0, 2, 1, 3)  # [j, s, h, i]
-    v_view = halves[:, 1].reshape(nb_total, hkv, d, bs).transpose(0, 3, 1, 2)  # [j, s, h, i]
+    # K: [j][h][i/8][s][i%8] -> [j][s][h][i/8][i%8]
+    k_view = halves[:, 0].reshape(nb_total, hkv, d // 8, bs, 8).transpose(0, 3, 1, 2, 4)
+    # V: [j][h][s/4][i][s%4] -> [j][s/4][s%4][h][i]
+    v_view = halves[:, 1].reshape(nb_total, hkv, bs // 4, d, 4).transpose(0, 2, 4, 1, 3)
     bad = ~valid
     k_view[bad] = nan_value(dtype)
-    v_view[bad] = nan_value(dtype)
+    v_view[bad.reshape(nb_total, bs // 4, 4)] = nan_value(dtype)
     return pool
 
 
