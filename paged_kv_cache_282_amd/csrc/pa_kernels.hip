@@ -884,6 +884,13 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 // M* = max M_j, L* = sum L_j 2^(M_j - M*), o = sum O_j 2^(M_j - M*) / L*.
 template <int D, int BS, typename OutT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  // One workgroup per (sequence, kv head) with more than one partition. Each
+  // 32-lane group reduces one row's partition maxima and sums; then every
+  // thread combines four output dimensions of one row over all partitions,
+  // with the partition weights taken from LDS in chunks.
+  constexpr int kChunk = 128;  // partitions whose weights are staged at once
+  __shared__ float s_w[kMaxGroup][kChunk];
+  __shared__ float s_max[kMaxGroup], s_inv[kMaxGroup];
   const int bg = blockIdx.x;
   if (bg >= a.num_seqs * a.hkv) return;
   const int b = bg / a.hkv, g = bg - b * a.hkv;
@@ -895,22 +902,68 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   if (np <= 1) return;
   const int G = a.hq / a.hkv;
   const int64_t row0 = static_cast<int64_t>(b) * a.hq + g * G;
-  OutT* out = static_cast<OutT*>(a.out) + row0 * D;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int row = idx / D, dd = idx - row * D;
-    const float* mlr = a.ws_ml + (row0 + row) * a.np_max * 2;
-    const float* orow = a.ws_o + (row0 + row) * a.np_max * D + dd;
+  const int t = threadIdx.x;
+  const int lrow = t >> 5, l32 = t & 31;  // 8 groups of 32 lanes: one row each
+  // -- row maximum and normaliser -----------------------------------------------
+  if (lrow < G) {
+    const float* mlr = a.ws_ml + (row0 + lrow) * a.np_max * 2;
     float M = -__builtin_inff();
-    for (int pp = 0; pp < np; ++pp) M = fmaxf(M, mlr[2 * pp]);
-    float L = 0.f, O = 0.f;
-    if (M != -__builtin_inff()) {
-      for (int pp = 0; pp < np; ++pp) {
-        const float f = exp2_fast(mlr[2 * pp] - M);
-        L = fmaf(mlr[2 * pp + 1], f, L);
-        O = fmaf(orow[static_cast<int64_t>(pp) * D], f, O);
+    for (int pp = l32; pp < np; pp += 32) M = fmaxf(M, mlr[2 * pp]);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float L = 0.f;
+    if (M != -__builtin_inff())
+      for (int pp = l32; pp < np; pp += 32) L = fmaf(mlr[2 * pp + 1], exp2_fast(mlr[2 * pp] - M), L);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) L += __shfl_xor(L, o);
+    if (l32 == 0) {
+      s_max[lrow] = M;
+      s_inv[lrow] = L > 0.f ? 1.f / L : 0.f;
+    }
+  }
+  // -- weighted sum of the partial outputs ------------------------------------------
+  constexpr int C4 = D / 4;
+  const int row = t / C4, c4 = t - row * C4;  // this thread: row, dims 4*c4 .. +3
+  const bool mine = t < G * C4;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  const float* orow = a.ws_o + (row0 + (mine ? row : 0)) * a.np_max * D + 4 * c4;
+  for (int p0 = 0; p0 < np; p0 += kChunk) {
+    const int cn = min(kChunk, np - p0);
+    __syncthreads();  // s_max ready; previous chunk's weights consumed
+    if (lrow < G) {
+      const float* mlr = a.ws_ml + (row0 + lrow) * a.np_max * 2;
+      const float M = s_max[lrow];
+      for (int k = l32; k < cn; k += 32)
+        s_w[lrow][k] = (M == -__builtin_inff()) ? 0.f : exp2_fast(mlr[2 * (p0 + k)] - M);
+    }
+    __syncthreads();
+    if (mine) {
+      int k = 0;
+      for (; k + 4 <= cn; k += 4) {  // four partials in flight
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          v[u] = *reinterpret_cast<const f32x4*>(orow + static_cast<int64_t>(p0 + k + u) * D);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = s_w[row][k + u];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) O[x] = fmaf(v[u][x], w, O[x]);
+        }
+      }
+      for (; k < cn; ++k) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(orow + static_cast<int64_t>(p0 + k) * D);
+        const float w = s_w[row][k];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) O[x] = fmaf(v[x], w, O[x]);
       }
     }
-    store_out<OutT>(out + idx, L > 0.f ? O / L : 0.f);
+  }
+  if (mine) {
+    const float inv = s_inv[row];
+    OutT* out = static_cast<OutT*>(a.out) + (row0 + row) * D + 4 * c4;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) store_out<OutT>(out + x, O[x] * inv);
   }
 }
 
