@@ -399,45 +399,56 @@ struct MergeSmem {
   float l[kWaves][kMaxGroup];
 };
 
-// Combines the kWaves states of row `row` at dimension `dd`: (M, L, O).
+// Combines the kWaves states of row `row` at dimensions dd .. dd+3: (M, L, O).
 template <int D>
 __device__ __forceinline__ void combine_waves(const MergeSmem<D>& sm, int row, int dd, float& M,
-                                              float& L, float& O) {
+                                              float& L, f32x4& O) {
   M = -__builtin_inff();
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][row]);
   L = 0.f;
-  O = 0.f;
+  O = f32x4{0.f, 0.f, 0.f, 0.f};
   if (M == -__builtin_inff()) return;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     const float f = exp2_fast(sm.m[w][row] - M);
+    const f32x4 ow = *reinterpret_cast<const f32x4*>(&sm.o[w][row][dd]);
     L = fmaf(sm.l[w][row], f, L);
-    O = fmaf(sm.o[w][row][dd], f, O);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) O[x] = fmaf(ow[x], f, O[x]);
   }
 }
 
 // After each wave has written its state: a single-partition sequence stores
 // its normalised output; otherwise this partition publishes (M, L, O) for the
 // merge kernel.
+//
+// Workspace layout: the partials of one (sequence, kv head) item are
+// contiguous, partition-major: O at ws_o[(p * rows + row) * D + d] and (M, L)
+// at ws_ml[(p * rows + row) * 2 + {0, 1}], from this (sequence, kv head)'s
+// base. A partition's rows x D partial is one contiguous run written with
+// 16-byte stores: scattered narrow writes into the workspace cost far more
+// HBM time than their bytes.
 template <int D, typename OutT>
 __device__ __forceinline__ void finish_partition(const MergeSmem<D>& sm, int rows, int np, int p,
-                                                 int np_max, OutT* __restrict__ out_rows,
+                                                 OutT* __restrict__ out_rows,
                                                  float* __restrict__ ws_o,
                                                  float* __restrict__ ws_ml) {
-  // out_rows: rows * D outputs; ws_o / ws_ml: this (sequence, group)'s first
-  // row's partials, rows spaced np_max * D (resp. np_max * 2) apart.
-  for (int idx = threadIdx.x; idx < rows * D; idx += kWaves * 64) {
-    const int row = idx / D, dd = idx - row * D;
-    float M, L, O;
+  constexpr int C4 = D / 4;
+  for (int c = threadIdx.x; c < rows * C4; c += kWaves * 64) {
+    const int row = c / C4, dd = 4 * (c - row * C4);
+    float M, L;
+    f32x4 O;
     combine_waves<D>(sm, row, dd, M, L, O);
     if (np == 1) {
-      store_out<OutT>(out_rows + idx, L > 0.f ? O / L : 0.f);
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) store_out<OutT>(out_rows + row * D + dd + x, O[x] * inv);
     } else {
-      ws_o[(static_cast<int64_t>(row) * np_max + p) * D + dd] = O;
+      *reinterpret_cast<f32x4*>(&ws_o[(static_cast<int64_t>(p) * rows + row) * D + dd]) = O;
       if (dd == 0) {
-        ws_ml[(static_cast<int64_t>(row) * np_max + p) * 2 + 0] = M;
-        ws_ml[(static_cast<int64_t>(row) * np_max + p) * 2 + 1] = L;
+        ws_ml[(static_cast<int64_t>(p) * rows + row) * 2 + 0] = M;
+        ws_ml[(static_cast<int64_t>(p) * rows + row) * 2 + 1] = L;
       }
     }
   }
@@ -539,7 +550,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   __syncthreads();
 
   const int64_t row0 = static_cast<int64_t>(it.b) * a.hq + it.g * G;
-  finish_partition<D, uint16_t>(sm, G, it.np, it.p, a.np_max,
+  finish_partition<D, uint16_t>(sm, G, it.np, it.p,
                                 static_cast<uint16_t*>(a.out) + row0 * D,
                                 a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2);
 }
@@ -771,10 +782,23 @@ void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
     eng.load_kv(buf, pool, a.blk_elems, kofs, vofs, pl.idA[s2], pl.idB[s2], lane, live);
   };
 
+  // The wave states of item i are merged and published while item i+1's
+  // steps are in flight (after its third and fourth steps' loads are issued),
+  // so that the merge never stands between a step's arrival and the next
+  // loads.
+  auto publish = [&](const MergeSmem<D>& sm, const QItem& it) {
+    const int64_t row0 = static_cast<int64_t>(it.b) * a.hq + it.g * G;
+    finish_partition<D, uint16_t>(sm, G, it.np, it.p,
+                                  static_cast<uint16_t*>(a.out) + row0 * D,
+                                  a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2);
+  };
+
   int cur_k = s_next[0], nxt_k = s_next[1];
   __syncthreads();  // both slots read before either is rewritten
   int parity = 0;
   Plan cur, nxt;
+  QItem prev;  // the item whose states wait in sm2[parity ^ 1]
+  bool have_prev = false;
   bf16x8 qcur[KS], qnxt[KS];
   plan_item(cur_k, cur, qcur);
   issue(cur, 0, kv[0]);
@@ -800,11 +824,12 @@ void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
         issue(cur, s2 + 2, kv[s2 & 1]);
       else
         issue(nxt, s2 + 2 - kSteps, kv[s2 & 1]);
+      if (s2 == 1 && have_prev) publish(sm2[parity ^ 1], prev);
     }
-    // -- merge the waves of the current item, publish --------------------------
+    // -- leave the wave states of the current item ---------------------------------
     // One barrier per item: the wave states and the queue slot alternate
-    // between two LDS copies, so item i+2 reuses item i's copy only after
-    // every thread has passed item i+1's barrier, i.e. finished item i.
+    // between two LDS copies. Item i's copy is read (published) during item
+    // i+1 and rewritten by item i+2, after item i+1's barrier.
     MergeSmem<D>& sm = sm2[parity];
     const float lt = sum_over_groups(eng.l[0]);
     if (r < G) {
@@ -818,10 +843,8 @@ void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
     }
     __syncthreads();
     const int after_k = s_next[parity];
-    const int64_t row0 = static_cast<int64_t>(cur.it.b) * a.hq + cur.it.g * G;
-    finish_partition<D, uint16_t>(sm, G, cur.it.np, cur.it.p, a.np_max,
-                                  static_cast<uint16_t*>(a.out) + row0 * D,
-                                  a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2);
+    prev = cur.it;
+    have_prev = true;
     parity ^= 1;
     cur = nxt;
 #pragma unroll
@@ -829,6 +852,7 @@ void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
     cur_k = nxt_k;
     nxt_k = after_k;
   }
+  if (have_prev) publish(sm2[parity ^ 1], prev);
   if (threadIdx.x == 0) {
     const int done = atomicAdd(&queue[1], 1);
     if (done == static_cast<int>(gridDim.x) - 1) {  // everyone else has left
@@ -875,7 +899,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  finish_partition<D, float>(sm, G, it.np, it.p, a.np_max, static_cast<float*>(a.out) + row0 * D,
+  finish_partition<D, float>(sm, G, it.np, it.p, static_cast<float*>(a.out) + row0 * D,
                              a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2);
 }
 
@@ -906,14 +930,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int lrow = t >> 5, l32 = t & 31;  // 8 groups of 32 lanes: one row each
   // -- row maximum and normaliser -----------------------------------------------
   if (lrow < G) {
-    const float* mlr = a.ws_ml + (row0 + lrow) * a.np_max * 2;
+    const float* mlr = a.ws_ml + row0 * a.np_max * 2 + 2 * lrow;  // partition pp at 2 * G * pp
     float M = -__builtin_inff();
-    for (int pp = l32; pp < np; pp += 32) M = fmaxf(M, mlr[2 * pp]);
+    for (int pp = l32; pp < np; pp += 32) M = fmaxf(M, mlr[2 * G * pp]);
 #pragma unroll
     for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     float L = 0.f;
     if (M != -__builtin_inff())
-      for (int pp = l32; pp < np; pp += 32) L = fmaf(mlr[2 * pp + 1], exp2_fast(mlr[2 * pp] - M), L);
+      for (int pp = l32; pp < np; pp += 32)
+        L = fmaf(mlr[2 * G * pp + 1], exp2_fast(mlr[2 * G * pp] - M), L);
 #pragma unroll
     for (int o = 16; o > 0; o >>= 1) L += __shfl_xor(L, o);
     if (l32 == 0) {
@@ -926,15 +951,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int row = t / C4, c4 = t - row * C4;  // this thread: row, dims 4*c4 .. +3
   const bool mine = t < G * C4;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
-  const float* orow = a.ws_o + (row0 + (mine ? row : 0)) * a.np_max * D + 4 * c4;
+  // partition pp of this row at orow + pp * G * D
+  const float* orow = a.ws_o + row0 * a.np_max * D + (mine ? row : 0) * D + 4 * c4;
   for (int p0 = 0; p0 < np; p0 += kChunk) {
     const int cn = min(kChunk, np - p0);
     __syncthreads();  // s_max ready; previous chunk's weights consumed
     if (lrow < G) {
-      const float* mlr = a.ws_ml + (row0 + lrow) * a.np_max * 2;
+      const float* mlr = a.ws_ml + row0 * a.np_max * 2 + 2 * lrow;
       const float M = s_max[lrow];
       for (int k = l32; k < cn; k += 32)
-        s_w[lrow][k] = (M == -__builtin_inff()) ? 0.f : exp2_fast(mlr[2 * (p0 + k)] - M);
+        s_w[lrow][k] = (M == -__builtin_inff()) ? 0.f : exp2_fast(mlr[2 * G * (p0 + k)] - M);
     }
     __syncthreads();
     if (mine) {
@@ -943,7 +969,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         f32x4 v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          v[u] = *reinterpret_cast<const f32x4*>(orow + static_cast<int64_t>(p0 + k + u) * D);
+          v[u] = *reinterpret_cast<const f32x4*>(orow + static_cast<int64_t>(p0 + k + u) * G * D);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const float w = s_w[row][k + u];
@@ -952,7 +978,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         }
       }
       for (; k < cn; ++k) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(orow + static_cast<int64_t>(p0 + k) * D);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(orow + static_cast<int64_t>(p0 + k) * G * D);
         const float w = s_w[row][k];
 #pragma unroll
         for (int x = 0; x < 4; ++x) O[x] = fmaf(v[x], w, O[x]);
@@ -1091,7 +1117,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
     }
   }
   __syncthreads();
-  finish_partition<D, float>(sm, G, 1, 0, 1, static_cast<float*>(a.out) + row0 * D, nullptr,
+  finish_partition<D, float>(sm, G, 1, 0, static_cast<float*>(a.out) + row0 * D, nullptr,
                              nullptr);
 }
 
