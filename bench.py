@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-attention hot path on one MI355X.
 
-Workload (default): the GQA long-tail decode batch -- 256 sequences, 64 query
+Headline workload: the GQA long-tail decode batch -- 256 sequences, 64 query
 heads / 8 KV heads, head_dim 128, block_size 16, bfloat16 with float32
 accumulation, context lengths lognormal (median 800, ln-sigma 1) clipped to
 [16, 8192], blocks placed by a seeded random permutation.
@@ -14,13 +14,21 @@ every sequence's new token (pa_append_kv) and run paged decode attention
 Reported (one JSON line on stdout):
   value      effective KV bandwidth = algorithmic K+V bytes attended / time, GB/s
              (each attended token's K and V read once per (sequence, kv head))
-  roofline   the decode kernel alone: algorithmic bytes per launch / its mean
-             duration (HIP events on the launch stream), against 8 TB/s
-  cpu_baseline  the fp64 NumPy oracle on one full layer on the host, 1 thread
+  roofline   pa_decode on the headline batch: algorithmic bytes per call / its
+             mean duration (HIP events on the launch stream around the call,
+             which runs the partition kernel and the split-K merge kernel),
+             against 8 TB/s; `traffic` is the HBM bytes per call measured with
+             rocprofv3 counters for this exact kernel source (null otherwise)
+  rows       every step of the hot path on its own workload: append, block copy,
+             decode on the other batches, chunked prefill -- time, algorithmic
+             bytes or flops, fraction of the matching roofline, and the oracle's
+             rate on a bounded sample of the same inputs
+  cpu_baseline  the fp64 NumPy oracle on one full headline layer, 1 thread
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,7 +40,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
 METRIC = "paged decode attention: effective KV HBM GB/s (% of peak) and seq-layers/s"
 WORKLOAD_DESC = {
     "gqa": "GQA long-tail decode: 256 seqs, 64 q / 8 kv heads, head_dim 128, block_size 16, "
@@ -40,6 +49,9 @@ WORKLOAD_DESC = {
     "mha": "MHA decode (7B-like layer): 64 seqs, 32/32 heads, head_dim 128, block_size 16, "
            "bf16, context lengths uniform [128, 2048]",
 }
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_gqa_longtail_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_282_amd", "csrc", f)
+                  for f in ("pa_kernels.hip", "pa_launch.h", "pa_api.cpp")]
 
 
 def log(msg: str) -> None:
@@ -53,14 +65,76 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--workload", default="gqa", choices=sorted(WORKLOAD_DESC))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip every oracle timing (headline and rows)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the per-row measurements")
+    ap.add_argument("--repeats", type=int, default=20, help="timed calls per batch, per row")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the headline, copy half of the first layer's pool onto the "
+                         "other half with one pa_copy_blocks call (a copy of known size for "
+                         "scaling memory-traffic counters)")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per pa_decode call on the headline batch, from the committed
+    rocprofv3 counter summary, if it was taken on the kernel source built now."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith("RESULT "):
+                    rec = json.loads(line[len("RESULT "):])
+                    if rec.get("kernel_source_sha256") == kernel_source_hash():
+                        return rec
+    except OSError:
+        pass
+    return None
 
 
 def to_dev(arr, dtype, torch):
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda().view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(arr, np.float32)).cuda()
+
+
+def i32(a, torch):
+    return torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+
+
+def time_calls(fn, torch, repeats: int, warmup: int = 3, batches: int = 5):
+    """Mean / p10 / p90 duration (ms) per call of fn().
+
+    Calls run back to back in `batches` batches of `repeats` calls, with HIP
+    events on the launch stream around each batch, so that short kernels are
+    not timed together with the host's launch latency.
+    """
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(batches)]
+    for a, b in ev:
+        a.record()
+        for _ in range(repeats):
+            fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) / repeats for a, b in ev])
+    return float(t.mean()), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+
+def kv_bytes(w) -> float:
+    return float(w.context_lens.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim \
+        * w.elem_bytes
 
 
 def cpu_baseline(w, gpu_out0: np.ndarray) -> dict:
@@ -75,14 +149,187 @@ def cpu_baseline(w, gpu_out0: np.ndarray) -> dict:
         ref = oracle.decode(w.q, pool_after, w.block_tables, w.context_lens, w.num_kv_heads,
                             w.block_size, w.scale, w.dtype)
         dt = time.perf_counter() - t0
-    kv_bytes = float(w.context_lens.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim \
-        * w.elem_bytes
     err = float(np.abs(gpu_out0 - ref).max())
-    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(kv_bytes(w) / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"one full layer: append of {w.num_seqs} tokens + decode of all "
                       f"{w.num_seqs} sequences, fp64 NumPy, 1 BLAS thread",
             "seconds": round(dt, 3), "seq_layers_per_s": round(w.num_seqs / dt, 2),
             "gpu_vs_oracle_max_abs_err": err}
+
+
+# -- per-row measurements -------------------------------------------------------------
+
+class Rows:
+    """Each step of the hot path on its own workload, against its own roofline."""
+
+    def __init__(self, pa, torch, repeats: int, oracle_on: bool):
+        self.pa, self.torch, self.repeats, self.oracle_on = pa, torch, repeats, oracle_on
+        self.out = {}
+
+    def _oracle(self, fn, amount: float, unit: str, sample: str) -> dict | None:
+        if not self.oracle_on:
+            return None
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            fn()
+            dt = time.perf_counter() - t0
+        return {"value": round(amount / dt, 4), "unit": unit, "cores": 1, "kind": "oracle",
+                "sample": sample, "seconds": round(dt, 3)}
+
+    def _record(self, key, kernel, workload, ms, amount, unit, peak, bound, oracle=None, **extra):
+        mean, p10, p90 = ms
+        scale = 1e9 if unit == "GB/s" else 1e12
+        achieved = amount / (mean * 1e-3) / scale
+        self.out[key] = {"kernel": kernel, "workload": workload,
+                         "us": round(mean * 1e3, 2), "us_p10": round(p10 * 1e3, 2),
+                         "us_p90": round(p90 * 1e3, 2),
+                         "algorithmic": amount, "achieved": round(achieved, 2), "unit": unit,
+                         "peak": peak, "bound": bound, "frac": round(achieved / peak, 4),
+                         "cpu_oracle": oracle, **extra}
+        log(f"  {key:28s} {mean * 1e3:9.1f} us  {achieved:9.1f} {unit}  "
+            f"({100 * achieved / peak:.1f}% of {peak:.0f})")
+
+    def device(self, w):
+        t, pa = self.torch, self.pa
+        d = {"pool": to_dev(w.pool, w.dtype, t), "q": to_dev(w.q, w.dtype, t),
+             "k_new": to_dev(w.k_new, w.dtype, t), "v_new": to_dev(w.v_new, w.dtype, t),
+             "slots": i32(w.slot_mapping, t), "tables": i32(w.block_tables, t),
+             "lens": i32(w.context_lens, t), "pairs": i32(w.copy_pairs.reshape(-1, 2), t)}
+        d["out"] = t.empty_like(d["q"])
+        d["ws"] = pa.new_decode_workspace(w.num_seqs, w.num_q_heads, w.head_dim,
+                                          w.max_context_len)
+        return d
+
+    def decode_row(self, key, w, d, desc, unique_bytes=None):
+        pa = self.pa
+
+        def call():
+            pa.pa_decode(d["out"], d["q"], d["pool"], d["tables"], d["lens"], w.max_context_len,
+                         w.num_kv_heads, w.block_size, w.scale, d["ws"])
+
+        ms = time_calls(call, self.torch, self.repeats)
+        n = min(16, w.num_seqs)
+        sample_bytes = float(w.context_lens[:n].astype(np.int64).sum()) * 2 * w.num_kv_heads \
+            * w.head_dim * w.elem_bytes
+
+        def orc():
+            import oracle
+            oracle.decode(w.q[:n], w.pool, w.block_tables[:n], w.context_lens[:n],
+                          w.num_kv_heads, w.block_size, w.scale, w.dtype)
+
+        extra = {}
+        if unique_bytes is not None:
+            extra["unique_bytes"] = unique_bytes
+            extra["achieved_unique"] = round(unique_bytes / (ms[0] * 1e-3) / 1e9, 2)
+        self._record(key, "pa_decode", desc, ms, kv_bytes(w), "GB/s", HBM_PEAK_GBS, "hbm",
+                     self._oracle(orc, sample_bytes / 1e9, "GB/s",
+                                  f"decode of the first {n} sequences (pool after the step's "
+                                  f"copy and append), fp64 NumPy, 1 BLAS thread"), **extra)
+
+    def run(self, make_workload):
+        import oracle
+        pa = self.pa
+
+        # -- shared-prefix batch: copy-on-write, then decode over shared blocks ----------
+        w = make_workload("prefix")
+        d = self.device(w)
+        blk_bytes = w.block_elems * w.elem_bytes
+        P = len(w.copy_pairs)
+
+        def copy():
+            pa.pa_copy_blocks(d["pool"], d["pairs"], w.num_kv_heads, w.head_dim, w.block_size)
+
+        copy()
+        ms = time_calls(copy, self.torch, self.repeats)
+        self._record("a2_copy_blocks", "pa_copy_blocks",
+                     f"shared-prefix CoW: {P} pairs of {blk_bytes // 1024} KiB blocks", ms,
+                     2.0 * P * blk_bytes, "GB/s", HBM_PEAK_GBS, "hbm",
+                     self._oracle(lambda: oracle.copy_blocks(w.pool, w.copy_pairs),
+                                  2.0 * P * blk_bytes / 1e9, "GB/s",
+                                  f"all {P} pairs, NumPy block copy (the oracle snapshots the pool first), 1 thread"))
+        pa.pa_append_kv(d["pool"], d["k_new"], d["v_new"], d["slots"], w.block_size)
+        self.torch.cuda.synchronize()
+        pool_np = oracle.copy_blocks(w.pool, w.copy_pairs)
+        pool_np = oracle.append(pool_np, w.k_new, w.v_new, w.slot_mapping, w.num_kv_heads,
+                                w.block_size, w.head_dim)
+        w.pool = pool_np  # the oracle sample below attends to the pool after the step
+        uniq = np.unique(np.concatenate([row[: -(-int(n) // w.block_size)]
+                                         for row, n in zip(w.block_tables, w.context_lens)]))
+        unique_bytes = float(len(uniq)) * blk_bytes
+        self.decode_row("a3_a7_decode_prefix", w, d,
+                        "shared-prefix decode: 32 prompts x 8 samples, prefix 1032, "
+                        "suffix U[1,512], 32 q / 8 kv heads, bf16", unique_bytes=unique_bytes)
+        del d, w, pool_np
+
+        # -- MHA batch ------------------------------------------------------------------------
+        w = make_workload("mha")
+        d = self.device(w)
+        pa.pa_append_kv(d["pool"], d["k_new"], d["v_new"], d["slots"], w.block_size)
+        w.pool = oracle.append(w.pool, w.k_new, w.v_new, w.slot_mapping, w.num_kv_heads,
+                               w.block_size, w.head_dim)
+        self.decode_row("a3_a7_decode_mha", w, d, WORKLOAD_DESC["mha"])
+        del d, w
+
+        # -- mixed iteration: append of 8432 tokens, decode, chunked prefill --------------
+        w = make_workload("mixed")
+        d = self.device(w)
+        T = len(w.slot_mapping)
+        row_bytes = T * w.num_kv_heads * w.head_dim * w.elem_bytes
+
+        def append():
+            pa.pa_append_kv(d["pool"], d["k_new"], d["v_new"], d["slots"], w.block_size)
+
+        append()
+        ms = time_calls(append, self.torch, self.repeats)
+        self._record("a1_append_kv", "pa_append_kv",
+                     f"mixed iteration: {T} new tokens (16 x 512 prefill + 240 decode), "
+                     "8 kv heads, head_dim 128, block_size 32, bf16", ms,
+                     4.0 * row_bytes, "GB/s", HBM_PEAK_GBS, "hbm",
+                     self._oracle(lambda: oracle.append(w.pool, w.k_new, w.v_new, w.slot_mapping,
+                                                        w.num_kv_heads, w.block_size, w.head_dim),
+                                  4.0 * row_bytes / 1e9, "GB/s",
+                                  f"all {T} tokens, NumPy scatter, 1 thread"),
+                     bytes_note="K and V rows read from k_new/v_new and written to the pool")
+        w.pool = oracle.append(w.pool, w.k_new, w.v_new, w.slot_mapping, w.num_kv_heads,
+                               w.block_size, w.head_dim)
+        self.decode_row("a3_a7_decode_mixed", w, d,
+                        "mixed iteration decode: 240 seqs U[256,4096], 32 q / 8 kv heads, "
+                        "head_dim 128, block_size 32, bf16")
+        pq = to_dev(w.prefill_q, w.dtype, self.torch)
+        pt, pl = i32(w.prefill_block_tables, self.torch), i32(w.prefill_context_lens, self.torch)
+        qsl = i32(w.query_start_loc, self.torch)
+        pout = self.torch.empty_like(pq)
+        Lc = np.diff(w.query_start_loc)
+        max_chunk = int(Lc.max())
+
+        def prefill():
+            pa.pa_prefill_chunk(pout, pq, d["pool"], pt, pl, qsl, max_chunk, w.num_kv_heads,
+                                w.block_size, w.scale)
+
+        ms = time_calls(prefill, self.torch, self.repeats)
+        keys = 0
+        for c in range(len(Lc)):
+            n, L = int(w.prefill_context_lens[c]), int(Lc[c])
+            keys += L * (n - L) + L * (L + 1) // 2  # query i attends to n - L + i + 1 keys
+        flops = 4.0 * w.head_dim * w.num_q_heads * keys
+
+        def orc():
+            oracle.prefill(w.prefill_q[: int(Lc[0])], w.pool, w.prefill_block_tables[:1],
+                           w.prefill_context_lens[:1], w.query_start_loc[:2], w.num_kv_heads,
+                           w.block_size, w.scale, w.dtype)
+
+        n0, L0 = int(w.prefill_context_lens[0]), int(Lc[0])
+        flops0 = 4.0 * w.head_dim * w.num_q_heads * (L0 * (n0 - L0) + L0 * (L0 + 1) // 2)
+        self._record("a8_prefill_chunk", "pa_prefill_chunk",
+                     f"mixed iteration prefill: {len(Lc)} chunks x {max_chunk} queries, prior "
+                     "U[0,2048], causal, 32 q / 8 kv heads, bf16", ms, flops, "TFLOP/s",
+                     MFMA_BF16_PEAK_TFLOPS, "mfma",
+                     self._oracle(orc, flops0 / 1e12, "TFLOP/s",
+                                  "chunk 0 only (512 queries), fp64 NumPy, 1 BLAS thread"),
+                     flops_note="4*d per (query, head, attended key): q.k and p.v")
+        del d, w, pq, pout
+        return self.out
 
 
 def main() -> int:
@@ -116,8 +363,8 @@ def main() -> int:
     q = to_dev(w.q, w.dtype, torch)
     k_new = to_dev(w.k_new, w.dtype, torch)
     v_new = to_dev(w.v_new, w.dtype, torch)
-    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()  # noqa: E731
-    slots, tables, lens = i32(w.slot_mapping), i32(w.block_tables), i32(w.context_lens)
+    slots, tables, lens = i32(w.slot_mapping, torch), i32(w.block_tables, torch), \
+        i32(w.context_lens, torch)
     outs = [torch.empty_like(q) for _ in range(L)]
     ws = pa.new_decode_workspace(w.num_seqs, w.num_q_heads, w.head_dim, w.max_context_len)
     max_ctx, hkv, bs, scale = w.max_context_len, w.num_kv_heads, w.block_size, w.scale
@@ -148,7 +395,7 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
-    # per-kernel durations (events on the launch stream around each call)
+    # per-call durations (events on the launch stream around each call)
     n = args.steps * L
     ea = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     eb = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -167,10 +414,10 @@ def main() -> int:
     dec_times = np.array([eb[k].elapsed_time(ec[k]) for k in range(n)])
     decode_ms = float(dec_times.mean())
 
-    kv_bytes_layer = float(w.context_lens.astype(np.int64).sum()) * 2 * hkv * w.head_dim \
-        * w.elem_bytes
+    kv_bytes_layer = kv_bytes(w)
     value = kv_bytes_layer * L / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes_layer / (decode_ms * 1e-3) / 1e9
+    traffic = measured_traffic() if args.workload == "gqa" else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -195,11 +442,15 @@ def main() -> int:
                        "pa_append_kv": round(append_ms, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "kernel": "decode_bf16_kernel<128,16> (pa_decode)",
+                     "traffic": None if traffic is None else traffic["hbm_bytes_per_call"],
+                     "kernel": "pa_decode = decode_bf16_persistent_kernel<128,16> + "
+                               "decode_merge_kernel<128,16,bf16>",
                      "algorithmic_bytes_per_launch": int(kv_bytes_layer)},
         "cpu_baseline": None,
     }
+    if traffic is not None:
+        result["roofline"]["traffic_detail"] = {k: traffic[k] for k in traffic
+                                                if k != "kernel_source_sha256"}
     log(f"step {ms_per_step:.3f} ms, decode {decode_ms * 1e3:.1f} us "
         f"({achieved:.0f} GB/s), append {append_ms * 1e3:.1f} us")
     if not args.no_cpu_baseline:
@@ -208,6 +459,22 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(w, gpu0)
         log(f"oracle: {result['cpu_baseline']['seconds']} s, "
             f"max abs err vs GPU {result['cpu_baseline']['gpu_vs_oracle_max_abs_err']:.3e}")
+    if args.calibrate_copy:
+        half = w.num_blocks // 2  # pairs (j, half + j): disjoint, inside the pool
+        pairs = torch.stack([torch.arange(half, dtype=torch.int32),
+                             torch.arange(half, 2 * half, dtype=torch.int32)], 1).contiguous().cuda()
+        torch.cuda.synchronize()
+        pa.pa_copy_blocks(pools[0], pairs, hkv, w.head_dim, bs)
+        torch.cuda.synchronize()
+        cal = half * w.block_elems * w.elem_bytes
+        result["calibration_copy"] = {"pairs": half, "bytes_read": cal, "bytes_written": cal}
+        log(f"calibration copy: {half} blocks, {cal / 1e6:.1f} MB read and written")
+    del pools, pool0, outs, ws
+    if not args.headline_only:
+        torch.cuda.empty_cache()
+        log("rows:")
+        result["rows"] = Rows(pa, torch, args.repeats, not args.no_cpu_baseline).run(
+            make_workload)
     print(json.dumps(result), flush=True)
     return 0
 

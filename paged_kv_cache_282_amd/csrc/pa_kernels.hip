@@ -1125,8 +1125,11 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
 // KV append and block copy (pure data movement).
 // ---------------------------------------------------------------------------
 // Thread -> (token, kv head, 8-element slice). K: the slice is one contiguous
-// 8-element run; V: its 8 dimensions sit 4 elements apart in the token's
-// 4-token slice.
+// 8-element run. V: the slice's 8 dimensions sit 4 elements apart in the
+// token's 4-slot slice. When four consecutive tokens of the list fill one
+// whole 4-slot slice (a prefill chunk does), the first of them writes the
+// slice's 8 dimensions for all four tokens as one contiguous run and the other
+// three write no V; otherwise each token writes its own V elements.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void append_kernel(T* __restrict__ pool,
                                                      const T* __restrict__ kn,
@@ -1135,6 +1138,8 @@ __global__ __launch_bounds__(256) void append_kernel(T* __restrict__ pool,
                                                      int num_tokens, int hkv, int bs,
                                                      int64_t blk_elems, int64_t num_slots) {
   constexpr int CH = D / 8;
+  constexpr int E16 = 16 / sizeof(T);  // elements per 16-byte word
+  constexpr int W = 8 / E16;           // 16-byte words per 8-element slice
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t per_tok = static_cast<int64_t>(hkv) * CH;
   const int64_t tok = gid / per_tok;
@@ -1145,23 +1150,50 @@ __global__ __launch_bounds__(256) void append_kernel(T* __restrict__ pool,
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / bs;
   const int off = slot - static_cast<int>(blk) * bs;
-  const int64_t src = (tok * hkv + h) * D + ch * 8;
   const int64_t tile = static_cast<int64_t>(h) * bs * D;
-  // K: slice ch of slot off; V: dims ch*8 .. +7 of slot off, 4 elements apart
-  T* kd = pool + blk * blk_elems + tile + (static_cast<int64_t>(ch) * bs + off) * 8;
-  T* vd = pool + blk * blk_elems + static_cast<int64_t>(hkv) * bs * D + tile +
-          (static_cast<int64_t>(off / 4) * D + ch * 8) * 4 + off % 4;
-  constexpr int W = 8 * sizeof(T) / 16;  // 16-byte words per chunk
+  // K: slice ch of slot off
+  {
+    const int64_t src = (tok * hkv + h) * D + ch * 8;
+    T* kd = pool + blk * blk_elems + tile + (static_cast<int64_t>(ch) * bs + off) * 8;
 #pragma unroll
-  for (int w = 0; w < W; ++w) st16(kd + w * (16 / sizeof(T)), ld16(kn + src + w * (16 / sizeof(T))));
+    for (int w = 0; w < W; ++w) st16(kd + w * E16, ld16(kn + src + w * E16));
+  }
+  // V: dims ch*8 .. +7 of the 4-slot slice off/4
+  T* vslice = pool + blk * blk_elems + static_cast<int64_t>(hkv) * bs * D + tile +
+              (static_cast<int64_t>(off / 4) * D + ch * 8) * 4;
+  const int r = off & 3;
+  const int64_t lead = tok - r;  // the token that would hold slot (slot - r)
+  bool quad = lead >= 0 && lead + 3 < num_tokens;
+  if (quad) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) quad = quad && slots[lead + k] == slot - r + k;
+  }
+  if (quad) {
+    if (r != 0) return;  // the slice's first token writes it
+    T v[4][8];           // [token][dim]
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t src = ((tok + k) * hkv + h) * D + ch * 8;
+#pragma unroll
+      for (int w = 0; w < W; ++w)
+        *reinterpret_cast<u32x4*>(&v[k][w * E16]) = ld16(vn + src + w * E16);
+    }
+    T t[8][4];  // [dim][token]: the slice's layout
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t[e][k] = v[k][e];
+    const T* tw = &t[0][0];
+#pragma unroll
+    for (int w = 0; w < 4 * W; ++w) st16(vslice + w * E16, *reinterpret_cast<const u32x4*>(tw + w * E16));
+    return;
+  }
+  const int64_t src = (tok * hkv + h) * D + ch * 8;
   T v[8];
 #pragma unroll
-  for (int w = 0; w < W; ++w) {
-    const u32x4 x = ld16(vn + src + w * (16 / sizeof(T)));
-    *reinterpret_cast<u32x4*>(&v[w * (16 / sizeof(T))]) = x;
-  }
+  for (int w = 0; w < W; ++w) *reinterpret_cast<u32x4*>(&v[w * E16]) = ld16(vn + src + w * E16);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) vd[4 * e] = v[e];
+  for (int e = 0; e < 8; ++e) vslice[4 * e + r] = v[e];
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ pool,
