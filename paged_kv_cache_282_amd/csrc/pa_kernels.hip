@@ -738,12 +738,18 @@ void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
   const int total = n_full_items + sc.part[B] * a.hkv;
 
   // Block ids of this wave's steps (0 for steps past the item's end) and the
-  // query slices of one item.
+  // query slices of one item. An item is planned one item ahead; its table
+  // entries (lanes 0 .. 2*kSteps-1 load one each) and query slices are loaded
+  // then but read only when its first loads are issued, after the current
+  // item's third step has been waited for. Vector loads complete in order, so
+  // by then those reads wait for nothing; reading them at once would wait for
+  // every KV load issued before them.
   struct Plan {
     QItem it;
+    int ent;  // lane l < 2*kSteps: table entry of step l/2, block A (l even) or B
     int idA[kSteps], idB[kSteps];
   };
-  auto plan_item = [&](int k, Plan& pl, bf16x8 (&qv)[KS]) {
+  auto plan_item = [&](int k, Plan& pl) {
     const bool live = k < total;
     if (live) {
       resolve_item(sc, B, a.hkv, n_full_items, k, pl.it);
@@ -752,24 +758,31 @@ void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
     }
     make_uniform(pl.it);
     const int32_t* trow = a.tables + static_cast<int64_t>(pl.it.b) * a.mb;
+    const int l = lane < 2 * kSteps ? lane : 0;
+    const int base =
+        (pl.it.tok0 + kStep * (wave + kWaves * (l >> 1))) / BS + (BS == 16 ? (l & 1) : 0);
+    pl.ent = trow[min(base, a.mb - 1)];
+  };
+  // Query rows g*G .. g*G+G-1 of an item, loaded right before the item's first
+  // KV loads, so that waiting for those covers these. Lanes past the group
+  // repeat row G-1: those padding rows are never stored, and they are fully
+  // masked wherever a step reaches past the context.
+  auto load_query = [&](const Plan& pl, bf16x8 (&qv)[KS]) {
+    const uint16_t* qr =
+        q + (static_cast<int64_t>(pl.it.b) * a.hq + pl.it.g * G + min(r, G - 1)) * D + 8 * kg;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) qv[s2] = __builtin_bit_cast(bf16x8, ld16(qr + 32 * s2));
+  };
+  auto block_ids = [&](Plan& pl) {
 #pragma unroll
     for (int s2 = 0; s2 < kSteps; ++s2) {
       const int t0 = pl.it.tok0 + kStep * (wave + kWaves * s2);
       const bool valid = t0 < pl.it.tok1;
-      const int base = t0 / BS;
-      const int ia = trow[min(base, a.mb - 1)];
-      const int ib = (BS == 16) ? trow[min(base + 1, a.mb - 1)] : ia;
+      const int ia = __builtin_amdgcn_readlane(pl.ent, 2 * s2);
+      const int ib = __builtin_amdgcn_readlane(pl.ent, 2 * s2 + 1);  // bs 32: unused
       pl.idA[s2] = valid ? clamp_block(ia, a.nb) : 0;
-      pl.idB[s2] = (valid && (BS == 32 || t0 + 16 < pl.it.tok1)) ? clamp_block(ib, a.nb)
-                                                                 : pl.idA[s2];
-    }
-    // query rows g*G .. g*G+G-1; lanes past the group read a valid row, then zero
-    const uint16_t* qr =
-        q + (static_cast<int64_t>(pl.it.b) * a.hq + pl.it.g * G + min(r, G - 1)) * D + 8 * kg;
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
-      const u32x4 w = ld16(qr + 32 * s2);
-      qv[s2] = __builtin_bit_cast(bf16x8, (r < G) ? w : u32x4{0u, 0u, 0u, 0u});
+      pl.idB[s2] = (valid && BS == 16 && t0 + 16 < pl.it.tok1) ? clamp_block(ib, a.nb)
+                                                                : pl.idA[s2];
     }
   };
   Eng eng;
@@ -800,11 +813,14 @@ void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
   QItem prev;  // the item whose states wait in sm2[parity ^ 1]
   bool have_prev = false;
   bf16x8 qcur[KS], qnxt[KS];
-  plan_item(cur_k, cur, qcur);
+  plan_item(cur_k, cur);
+  block_ids(cur);
+  load_query(cur, qcur);
   issue(cur, 0, kv[0]);
   issue(cur, 1, kv[1]);
   while (cur_k < total) {
-    plan_item(nxt_k, nxt, qnxt);
+    int after_id = 0;
+    plan_item(nxt_k, nxt);
     eng.init();
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) eng.qreg[0][s2] = qcur[s2];
@@ -815,10 +831,13 @@ void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
       const int t0 = cur.it.tok0 + kStep * (wave + kWaves * s2);
       if (t0 < cur.it.tok1) eng.compute(kv[s2 & 1], t0, cur.it.tok1, lane, a.sl2e);
       if (s2 == kSteps - 2 && threadIdx.x == 0) {
-        // Take the item after next. The result goes to LDS inside this branch:
-        // only this wave waits for it, at a point where its remaining loads of
-        // the current item are needed next anyway.
-        s_next[parity] = atomicAdd(&queue[0], 1);
+        // Take the item after next; the id goes to LDS just before the
+        // barrier, when waiting for it no longer holds back any load.
+        after_id = atomicAdd(&queue[0], 1);
+      }
+      if (s2 == kSteps - 2) {
+        block_ids(nxt);
+        load_query(nxt, qnxt);
       }
       if (s2 + 2 < kSteps)
         issue(cur, s2 + 2, kv[s2 & 1]);
@@ -830,6 +849,7 @@ void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
     // One barrier per item: the wave states and the queue slot alternate
     // between two LDS copies. Item i's copy is read (published) during item
     // i+1 and rewritten by item i+2, after item i+1's barrier.
+    if (threadIdx.x == 0) s_next[parity] = after_id;
     MergeSmem<D>& sm = sm2[parity];
     const float lt = sum_over_groups(eng.l[0]);
     if (r < G) {
