@@ -41,6 +41,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ constexpr bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
+// Block-table entry read through the scalar cache (the row pointer and index
+// are wave-uniform; the tables are not written while a kernel runs). Scalar
+// loads are counted apart from vector loads, so waiting for a table entry
+// never waits for KV loads issued earlier.
+typedef const __attribute__((address_space(4))) int32_t* table_ptr;
+__device__ __forceinline__ int table_entry(const int32_t* row, int idx) {
+  return ((table_ptr)row)[idx];  // address-space cast
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ u32x4 ld16(const void* p) {
@@ -1041,22 +1050,40 @@ __device__ __forceinline__ bool chunk_geometry(const PrefillArgs& a, int c, int 
 }
 
 // bf16: a wave owns NT tiles of 16 rows; row R -> (position R / G, head R % G).
+// The workgroup's four waves cover consecutive positions and share one key
+// range, so each 32-token step of K and V is loaded from HBM once per
+// workgroup (16-byte loads by all 256 threads, issued a step ahead) into one of
+// two LDS buffers, and every wave reads its MFMA operands from there.
+template <int D>
+struct PrefillSmem {
+  uint16_t k[2][(D / 8) * kStep * 8];        // [slice][token][8], tokens of one step
+  uint16_t v[2][(kStep / 4) * D * 4];        // [4-token slice][dim][4]
+};
+
 template <int D, int BS, int NT>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_bf16_kernel(PrefillArgs a) {
+  using Eng = Bf16Engine<D, BS, NT>;
+  constexpr int KS = Eng::KS, VT = Eng::VT;
+  constexpr int kChunks = 2 * D * kStep * 2 / 16;  // 16-byte pieces of one step's K and V
+  constexpr int kPer = kChunks / 256;              // per thread
+  static_assert(kChunks % 256 == 0, "a step is a whole number of 16-byte pieces per thread");
+  __shared__ PrefillSmem<D> sm;
   const int c = blockIdx.y, g = blockIdx.z;
   int q0, L, prior;
-  if (!chunk_geometry(a, c, a.mb * BS, q0, L, prior)) return;
+  if (!chunk_geometry(a, c, a.mb * BS, q0, L, prior)) return;  // uniform per workgroup
   const int G = a.hq / a.hkv;
   const int pos_per_wave = 16 * NT / G;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int i0 = (blockIdx.x * kWaves + wave) * pos_per_wave;
-  if (i0 >= L) return;
+  const int wg_i0 = blockIdx.x * kWaves * pos_per_wave;
+  if (wg_i0 >= L) return;  // uniform per workgroup
+  const int i0 = wg_i0 + wave * pos_per_wave;
   const int r = lane & 15, kg = lane >> 4;
   const uint16_t* pool = static_cast<const uint16_t*>(a.pool);
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
 
-  Bf16Engine<D, BS, NT> eng;
+  Eng eng;
   eng.init();
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -1067,15 +1094,80 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a) {
       eng.lim[nt] = prior + i;
     }
   }
-  const int imax = min(L - 1, i0 + pos_per_wave - 1);
-  const int kend = prior + imax + 1;
+  // keys 0 .. kend-1 for this wave's rows, kend_wg for the workgroup's
+  const int kend = prior + min(L, i0 + pos_per_wave);
+  const int kend_wg = prior + min(L, wg_i0 + kWaves * pos_per_wave);
+  const int32_t* trow = a.tables + static_cast<int64_t>(c) * a.mb;
   const int64_t kofs = static_cast<int64_t>(g) * BS * D;
   const int64_t vofs = static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(g) * D * BS;
-  const int32_t* trow = a.tables + static_cast<int64_t>(c) * a.mb;
-  for (int t0 = 0; t0 < kend; t0 += kStep) {
-    int blkA, blkB;
-    step_blocks<BS>(trow, t0, kend, a.nb, blkA, blkB);
-    eng.step(pool, a.blk_elems, kofs, vofs, blkA, blkB, t0, kend, lane, a.sl2e);
+
+  // Piece p of a step: K pieces first ([slice c][token t], one token's 8
+  // dims), then V pieces ([4-token slice s][dim pair], 2 dims x 4 tokens).
+  // Returns the element offset inside the step's block (A: tokens 0..15 or,
+  // at bs 32, all 32) and whether it comes from block B (bs 16, tokens 16..31).
+  auto piece_src = [&](int pc, bool& from_b) -> int64_t {
+    if (pc < kChunks / 2) {
+      const int sl = pc / kStep, t = pc - sl * kStep;
+      from_b = BS == 16 && t >= 16;
+      const int slot = BS == 16 ? (t & 15) : t;
+      return kofs + (static_cast<int64_t>(sl) * BS + slot) * 8;
+    }
+    const int pv = pc - kChunks / 2;
+    const int sl = pv / (D / 2), dp = pv - sl * (D / 2);
+    from_b = BS == 16 && sl >= 4;
+    const int bsl = BS == 16 ? (sl & 3) : sl;
+    return vofs + (static_cast<int64_t>(bsl) * D + 2 * dp) * 4;
+  };
+  u32x4 pre[kPer];
+  auto fetch = [&](int t0) {  // step at t0 -> registers (t0 < kend_wg)
+    const int ia = table_entry(trow, t0 / BS);
+    const int ib = (BS == 16 && t0 + 16 < kend_wg) ? table_entry(trow, t0 / BS + 1) : ia;
+    const uint16_t* bA = pool + clamp_block(ia, a.nb) * a.blk_elems;
+    const uint16_t* bB = pool + clamp_block(ib, a.nb) * a.blk_elems;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      bool from_b;
+      const int64_t off = piece_src(u * 256 + static_cast<int>(threadIdx.x), from_b);
+      pre[u] = ld16((from_b ? bB : bA) + off);
+    }
+  };
+  auto stash = [&](int buf) {  // registers -> LDS buffer
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int pc = u * 256 + static_cast<int>(threadIdx.x);
+      uint16_t* dst = pc < kChunks / 2 ? &sm.k[buf][pc * 8] : &sm.v[buf][(pc - kChunks / 2) * 8];
+      *reinterpret_cast<u32x4*>(dst) = pre[u];
+    }
+  };
+  auto operands = [&](int buf, typename Eng::KV& kv) {  // LDS -> this lane's MFMA operands
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      kv.kA[s2] = *reinterpret_cast<const u32x4*>(&sm.k[buf][((4 * s2 + kg) * kStep + r) * 8]);
+      kv.kB[s2] = *reinterpret_cast<const u32x4*>(&sm.k[buf][((4 * s2 + kg) * kStep + 16 + r) * 8]);
+    }
+#pragma unroll
+    for (int j = 0; j < VT; ++j) {
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(&sm.v[buf][(kg * D + 16 * j + r) * 4]);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(&sm.v[buf][((4 + kg) * D + 16 * j + r) * 4]);
+      kv.vv[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  int buf = 0;
+  for (int t0 = 0; t0 < kend_wg; t0 += kStep) {
+    const bool more = t0 + kStep < kend_wg;
+    if (more) fetch(t0 + kStep);
+    if (i0 < L && t0 < kend) {  // this wave has rows, and they see keys of this step
+      typename Eng::KV kv;
+      operands(buf, kv);
+      eng.compute(kv, t0, kend_wg, lane, a.sl2e);
+    }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
   }
   uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
