@@ -94,13 +94,31 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
 
+// Four consecutive values as one store: 16 bytes of float or 8 of bf16.
 template <typename T>
-__device__ __forceinline__ void store_out(T* p, float v);
+__device__ __forceinline__ void store4(T* p, f32x4 v);
 template <>
-__device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
 template <>
-__device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
-  *p = f32_to_bf16_bits(v);
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4 v) {
+  u32x2 w;
+  w[0] = f32_to_bf16_bits(v[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+  w[1] = f32_to_bf16_bits(v[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+  *reinterpret_cast<u32x2*>(p) = w;
+}
+template <typename T>
+__device__ __forceinline__ f32x4 load4(const T* p);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 load4<uint16_t>(const uint16_t* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+               __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
 }
 
 __device__ __forceinline__ int clamp_block(int blk, int64_t nb) {
@@ -429,19 +447,21 @@ __device__ __forceinline__ void combine_waves(const MergeSmem<D>& sm, int row, i
 }
 
 // After each wave has written its state: a single-partition sequence stores
-// its normalised output; otherwise this partition publishes (M, L, O) for the
-// merge kernel.
+// its normalised output; otherwise this partition publishes (M, L, o) for the
+// merge kernel, where o = O / L is the partition's own normalised output,
+// rounded to the output type like a final row.
 //
 // Workspace layout: the partials of one (sequence, kv head) item are
-// contiguous, partition-major: O at ws_o[(p * rows + row) * D + d] and (M, L)
-// at ws_ml[(p * rows + row) * 2 + {0, 1}], from this (sequence, kv head)'s
-// base. A partition's rows x D partial is one contiguous run written with
-// 16-byte stores: scattered narrow writes into the workspace cost far more
-// HBM time than their bytes.
+// contiguous, partition-major: o at ws_o[(p * rows + row) * D + d] (elements
+// of OutT) and (M, L) at ws_ml[(p * rows + row) * 2 + {0, 1}] (float), from
+// this (sequence, kv head)'s base. A partition's rows x D partial is one
+// contiguous run written with 8- or 16-byte stores. These writes, interleaved
+// with the stream of K/V reads, cost several times their bytes in HBM time,
+// so a bf16 call keeps its partials in bf16: half the bytes of float.
 template <int D, typename OutT>
 __device__ __forceinline__ void finish_partition(const MergeSmem<D>& sm, int rows, int np, int p,
                                                  OutT* __restrict__ out_rows,
-                                                 float* __restrict__ ws_o,
+                                                 OutT* __restrict__ ws_o,
                                                  float* __restrict__ ws_ml) {
   constexpr int C4 = D / 4;
   for (int c = threadIdx.x; c < rows * C4; c += kWaves * 64) {
@@ -449,12 +469,11 @@ __device__ __forceinline__ void finish_partition(const MergeSmem<D>& sm, int row
     float M, L;
     f32x4 O;
     combine_waves<D>(sm, row, dd, M, L, O);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
     if (np == 1) {
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) store_out<OutT>(out_rows + row * D + dd + x, O[x] * inv);
+      store4<OutT>(out_rows + row * D + dd, O * inv);
     } else {
-      *reinterpret_cast<f32x4*>(&ws_o[(static_cast<int64_t>(p) * rows + row) * D + dd]) = O;
+      store4<OutT>(ws_o + (static_cast<int64_t>(p) * rows + row) * D + dd, O * inv);
       if (dd == 0) {
         ws_ml[(static_cast<int64_t>(p) * rows + row) * 2 + 0] = M;
         ws_ml[(static_cast<int64_t>(p) * rows + row) * 2 + 1] = L;
@@ -472,7 +491,7 @@ struct DecodeArgs {
   int num_seqs, mb, hq, hkv, max_ctx, np_max, n_items;
   int64_t nb, blk_elems;
   float sl2e;
-  float* ws_o;
+  void* ws_o;  // partial outputs, elements of the output type
   float* ws_ml;
 };
 
@@ -561,7 +580,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
   const int64_t row0 = static_cast<int64_t>(it.b) * a.hq + it.g * G;
   finish_partition<D, uint16_t>(sm, G, it.np, it.p,
                                 static_cast<uint16_t*>(a.out) + row0 * D,
-                                a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2);
+                                static_cast<uint16_t*>(a.ws_o) + row0 * a.np_max * D,
+                                a.ws_ml + row0 * a.np_max * 2);
 }
 
 // ---------------------------------------------------------------------------
@@ -812,7 +832,8 @@ void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
     const int64_t row0 = static_cast<int64_t>(it.b) * a.hq + it.g * G;
     finish_partition<D, uint16_t>(sm, G, it.np, it.p,
                                   static_cast<uint16_t*>(a.out) + row0 * D,
-                                  a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2);
+                                  static_cast<uint16_t*>(a.ws_o) + row0 * a.np_max * D,
+                                  a.ws_ml + row0 * a.np_max * 2);
   };
 
   int cur_k = s_next[0], nxt_k = s_next[1];
@@ -929,12 +950,14 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
   }
   __syncthreads();
   finish_partition<D, float>(sm, G, it.np, it.p, static_cast<float*>(a.out) + row0 * D,
-                             a.ws_o + row0 * a.np_max * D, a.ws_ml + row0 * a.np_max * 2);
+                             static_cast<float*>(a.ws_o) + row0 * a.np_max * D,
+                             a.ws_ml + row0 * a.np_max * 2);
 }
 
 // Split-K merge: one workgroup per (sequence, kv head) with more than one
-// partition combines the partitions' (M, L, O) by the log-sum-exp identity
-// M* = max M_j, L* = sum L_j 2^(M_j - M*), o = sum O_j 2^(M_j - M*) / L*.
+// partition combines the partitions' (M, L, o = O / L) by the log-sum-exp
+// identity M* = max M_j, L* = sum L_j 2^(M_j - M*),
+// out = sum L_j 2^(M_j - M*) o_j / L*.
 template <int D, int BS, typename OutT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   // One workgroup per (sequence, kv head) with more than one partition. Each
@@ -981,7 +1004,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const bool mine = t < G * C4;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
   // partition pp of this row at orow + pp * G * D
-  const float* orow = a.ws_o + row0 * a.np_max * D + (mine ? row : 0) * D + 4 * c4;
+  const OutT* orow =
+      static_cast<const OutT*>(a.ws_o) + row0 * a.np_max * D + (mine ? row : 0) * D + 4 * c4;
   for (int p0 = 0; p0 < np; p0 += kChunk) {
     const int cn = min(kChunk, np - p0);
     __syncthreads();  // s_max ready; previous chunk's weights consumed
@@ -989,7 +1013,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
       const float* mlr = a.ws_ml + row0 * a.np_max * 2 + 2 * lrow;
       const float M = s_max[lrow];
       for (int k = l32; k < cn; k += 32)
-        s_w[lrow][k] = (M == -__builtin_inff()) ? 0.f : exp2_fast(mlr[2 * G * (p0 + k)] - M);
+        s_w[lrow][k] = (M == -__builtin_inff())
+                           ? 0.f
+                           : mlr[2 * G * (p0 + k) + 1] * exp2_fast(mlr[2 * G * (p0 + k)] - M);
     }
     __syncthreads();
     if (mine) {
@@ -998,7 +1024,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         f32x4 v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          v[u] = *reinterpret_cast<const f32x4*>(orow + static_cast<int64_t>(p0 + k + u) * G * D);
+          v[u] = load4<OutT>(orow + static_cast<int64_t>(p0 + k + u) * G * D);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const float w = s_w[row][k + u];
@@ -1007,7 +1033,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         }
       }
       for (; k < cn; ++k) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(orow + static_cast<int64_t>(p0 + k) * G * D);
+        const f32x4 v = load4<OutT>(orow + static_cast<int64_t>(p0 + k) * G * D);
         const float w = s_w[row][k];
 #pragma unroll
         for (int x = 0; x < 4; ++x) O[x] = fmaf(v[x], w, O[x]);
@@ -1017,8 +1043,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   if (mine) {
     const float inv = s_inv[row];
     OutT* out = static_cast<OutT*>(a.out) + (row0 + row) * D + 4 * c4;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) store_out<OutT>(out + x, O[x] * inv);
+    store4<OutT>(out, O * inv);
   }
 }
 
@@ -1461,7 +1486,7 @@ hipError_t launch_decode(void* out, const void* q, const void* pool, const int32
   a.nb = ps.num_blocks;
   a.blk_elems = ps.block_elems();
   a.sl2e = scale * kLog2e;
-  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
+  a.ws_o = static_cast<char*>(workspace) + wl.o_off;
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
   int32_t* queue = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.queue_off);
   const int64_t items = static_cast<int64_t>(num_seqs) * ps.num_kv_heads * np_max;

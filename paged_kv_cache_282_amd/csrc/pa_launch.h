@@ -34,6 +34,7 @@ struct DecodeWorkspace {
     DecodeWorkspace w;
     w.queue_off = 0;
     w.o_off = 256;
+    // partial outputs are float or bf16 (the call's type); sized for float
     size_t o_bytes = size_t(num_seqs) * num_q_heads * max_parts * head_dim * sizeof(float);
     w.ml_off = w.o_off + up(o_bytes);
     size_t ml_bytes = size_t(num_seqs) * num_q_heads * max_parts * 2 * sizeof(float);
