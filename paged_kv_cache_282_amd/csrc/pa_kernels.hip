@@ -960,13 +960,14 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeArgs a) {
 // out = sum L_j 2^(M_j - M*) o_j / L*.
 template <int D, int BS, typename OutT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  // One workgroup per (sequence, kv head) with more than one partition. Each
-  // 32-lane group reduces one row's partition maxima and sums; then every
-  // thread combines four output dimensions of one row over all partitions,
-  // with the partition weights taken from LDS in chunks.
-  constexpr int kChunk = 128;  // partitions whose weights are staged at once
-  __shared__ float s_w[kMaxGroup][kChunk];
-  __shared__ float s_max[kMaxGroup], s_inv[kMaxGroup];
+  // One workgroup per (sequence, kv head) with more than one partition; each
+  // thread combines four output dimensions of one row. It reads the (M, L)
+  // of its row itself (the 32 or 16 threads of a row read the same words), so
+  // there is no barrier: the partials are read in batches of kBatch
+  // partitions, all loads of a batch issued together, and folded into a
+  // running (M, L, O) that is rescaled when a batch raises the maximum.
+  constexpr int C4 = D / 4;
+  constexpr int kBatch = 8;
   const int bg = blockIdx.x;
   if (bg >= a.num_seqs * a.hkv) return;
   const int b = bg / a.hkv, g = bg - b * a.hkv;
@@ -977,74 +978,44 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int np = (n + kPartition - 1) / kPartition;
   if (np <= 1) return;
   const int G = a.hq / a.hkv;
+  const int row = threadIdx.x / C4, c4 = threadIdx.x - row * C4;
+  if (row >= G) return;
   const int64_t row0 = static_cast<int64_t>(b) * a.hq + g * G;
-  const int t = threadIdx.x;
-  const int lrow = t >> 5, l32 = t & 31;  // 8 groups of 32 lanes: one row each
-  // -- row maximum and normaliser -----------------------------------------------
-  if (lrow < G) {
-    const float* mlr = a.ws_ml + row0 * a.np_max * 2 + 2 * lrow;  // partition pp at 2 * G * pp
-    float M = -__builtin_inff();
-    for (int pp = l32; pp < np; pp += 32) M = fmaxf(M, mlr[2 * G * pp]);
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float L = 0.f;
-    if (M != -__builtin_inff())
-      for (int pp = l32; pp < np; pp += 32)
-        L = fmaf(mlr[2 * G * pp + 1], exp2_fast(mlr[2 * G * pp] - M), L);
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) L += __shfl_xor(L, o);
-    if (l32 == 0) {
-      s_max[lrow] = M;
-      s_inv[lrow] = L > 0.f ? 1.f / L : 0.f;
-    }
-  }
-  // -- weighted sum of the partial outputs ------------------------------------------
-  constexpr int C4 = D / 4;
-  const int row = t / C4, c4 = t - row * C4;  // this thread: row, dims 4*c4 .. +3
-  const bool mine = t < G * C4;
+  // partition pp of this row: (M, L) at mlr[2 * G * pp], o at orow[pp * G * D]
+  const float* mlr = a.ws_ml + row0 * a.np_max * 2 + 2 * row;
+  const OutT* orow = static_cast<const OutT*>(a.ws_o) + row0 * a.np_max * D + row * D + 4 * c4;
+  float M = -__builtin_inff(), L = 0.f;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
-  // partition pp of this row at orow + pp * G * D
-  const OutT* orow =
-      static_cast<const OutT*>(a.ws_o) + row0 * a.np_max * D + (mine ? row : 0) * D + 4 * c4;
-  for (int p0 = 0; p0 < np; p0 += kChunk) {
-    const int cn = min(kChunk, np - p0);
-    __syncthreads();  // s_max ready; previous chunk's weights consumed
-    if (lrow < G) {
-      const float* mlr = a.ws_ml + row0 * a.np_max * 2 + 2 * lrow;
-      const float M = s_max[lrow];
-      for (int k = l32; k < cn; k += 32)
-        s_w[lrow][k] = (M == -__builtin_inff())
-                           ? 0.f
-                           : mlr[2 * G * (p0 + k) + 1] * exp2_fast(mlr[2 * G * (p0 + k)] - M);
+  for (int p0 = 0; p0 < np; p0 += kBatch) {
+    float2 ml[kBatch];
+    f32x4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {  // past the last partition: re-read it, unused
+      const int pp = min(p0 + u, np - 1);
+      ml[u] = *reinterpret_cast<const float2*>(mlr + 2 * G * pp);
+      v[u] = load4<OutT>(orow + static_cast<int64_t>(pp) * G * D);
     }
-    __syncthreads();
-    if (mine) {
-      int k = 0;
-      for (; k + 4 <= cn; k += 4) {  // four partials in flight
-        f32x4 v[4];
+    float bm = M;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          v[u] = load4<OutT>(orow + static_cast<int64_t>(p0 + k + u) * G * D);
+    for (int u = 0; u < kBatch; ++u)
+      if (p0 + u < np) bm = fmaxf(bm, ml[u].x);
+    if (bm == -__builtin_inff()) continue;
+    const float f = exp2_fast(M - bm);  // 0 while nothing is accumulated
+    L *= f;
+    O *= f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float w = s_w[row][k + u];
+    for (int u = 0; u < kBatch; ++u) {
+      if (p0 + u < np) {
+        const float w = ml[u].y * exp2_fast(ml[u].x - bm);
+        L += w;
 #pragma unroll
-          for (int x = 0; x < 4; ++x) O[x] = fmaf(v[u][x], w, O[x]);
-        }
-      }
-      for (; k < cn; ++k) {
-        const f32x4 v = load4<OutT>(orow + static_cast<int64_t>(p0 + k) * G * D);
-        const float w = s_w[row][k];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) O[x] = fmaf(v[x], w, O[x]);
+        for (int x = 0; x < 4; ++x) O[x] = fmaf(v[u][x], w, O[x]);
       }
     }
+    M = bm;
   }
-  if (mine) {
-    const float inv = s_inv[row];
-    OutT* out = static_cast<OutT*>(a.out) + (row0 + row) * D + 4 * c4;
-    store4<OutT>(out, O * inv);
-  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  store4<OutT>(static_cast<OutT*>(a.out) + (row0 + row) * D + 4 * c4, O * inv);
 }
 
 // ---------------------------------------------------------------------------
