@@ -1,0 +1,352 @@
+"""Plain-Python oracle of the host block manager and the iteration-level scheduler.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What the pages fix, and what this module restates:
+  * Static batching launches a fixed batch and releases it only when its
+    slowest member finishes; finished members leave their slot idle ("Module 4
+    · Batching, Scheduling, and Paging", section "Static batching: the batch
+    waits for its slowest member").
+  * Continuous batching reschedules every iteration: finished sequences leave
+    and waiting requests are admitted into the freed slots (same page, section
+    "Continuous batching: reschedule every iteration"; worksonmygpu.com post,
+    section "Iteration-level scheduling").
+  * Orca avoids running out of KV memory by reserving the maximum response
+    length for every admitted request (Module 4, "Continuous batching", the
+    tradeoff note; "Paging the KV Cache", section "The waste hiding inside
+    memory").
+  * PagedAttention allocates a block only when the previous one fills, frees
+    blocks when a request completes, and evicts a request (discard and
+    recompute later) when HBM runs out (Module 4, section "PagedAttention").
+  * Parallel samples share the prompt's blocks; the first divergent write into
+    a shared block copies it, and reference counts keep a block alive until its
+    last user is done (Module 4, section "Block sharing").
+  * Prefill and decode share an iteration under a policy that bounds the work
+    of one iteration (worksonmygpu.com post, section "The prefill/decode mix").
+
+Where the pages leave a step open, the reading taken here (each is listed in
+the design notes):
+  * one iteration has a token budget: decode tokens first (one per running
+    sample), then prefill chunks of at most ``max_chunk`` tokens, continuing
+    requests before admitting new ones;
+  * admission is first come, first served and never skips the head of the
+    queue; a request with n samples takes n batch slots from admission on;
+  * a decode sequence appends the KV of its previous token and produces the
+    next; a prompt's last prefill chunk produces every sample's first token;
+  * the free list is a stack: blocks are taken in ``free_order`` at first and
+    a released block is the next one taken;
+  * paged eviction: before any append of an iteration, while the free blocks
+    cannot cover what the running requests need this iteration (one block per
+    decode sample whose last block is full or shared, plus the blocks of each
+    continuing prefill chunk), the most recently admitted running request is
+    evicted: its blocks are released and it restarts from its prompt at the
+    head of the queue; an iteration that evicted admits nobody;
+  * reservation (Orca, and static batching) holds ceil(max_len / bs) blocks per
+    sample from admission until that sample finishes (static: until the batch
+    ends); without paging, samples do not share, so the prompt's blocks are
+    copied into each further sample's reservation before its first decode.
+"""
+from __future__ import annotations
+
+from collections import deque
+from dataclasses import dataclass, field
+
+POLICIES = ("paged", "reserve", "static")
+
+
+@dataclass
+class SchedConfig:
+    num_blocks: int
+    block_size: int
+    max_seqs: int      # batch slots: samples that may run at once
+    max_tokens: int    # tokens one iteration may process (decode + prefill)
+    max_chunk: int     # longest prefill chunk
+    max_len: int       # longest context a sample may reach (prompt + output - 1)
+    policy: str = "paged"
+
+
+@dataclass
+class Plan:
+    """What one iteration does, in launch order: copies, then appends, then attention."""
+    iteration: int
+    copies: list = field(default_factory=list)    # (src, dst) block pairs
+    slots: list = field(default_factory=list)     # prefill tokens (chunk order), then decode tokens
+    chunks: list = field(default_factory=list)    # (req, q_start, length, context_len, table)
+    decodes: list = field(default_factory=list)   # (req, sample, context_len, table)
+    admitted: list = field(default_factory=list)
+    preempted: list = field(default_factory=list)
+    finished: list = field(default_factory=list)
+    generated: int = 0
+
+
+class _Sample:
+    def __init__(self, table, ntok, out):
+        self.table = table
+        self.ntok = ntok      # tokens whose KV is cached
+        self.gen = 1          # tokens produced (the prefill produced the first)
+        self.out = out
+        self.done = out == 1
+        self.released = False
+
+
+class _Request:
+    def __init__(self, rid, prompt, outs, arrival):
+        self.rid = rid
+        self.prompt = int(prompt)
+        self.outs = [int(o) for o in outs]
+        self.arrival = int(arrival)
+        self.reset()
+        self.evictions = 0
+
+    def reset(self):
+        self.state = "waiting"
+        self.prefilled = 0
+        self.table = []        # the prompt's table while it is prefilled
+        self.reserved = []     # reservation tables of samples 1 .. n-1
+        self.samples = []
+
+    @property
+    def n(self):
+        return len(self.outs)
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+class Scheduler:
+    """Drives requests through prefill and decode, one ``step()`` per iteration.
+
+    ``requests`` is a list of (prompt_len, [output_len per sample], arrival_iteration),
+    in arrival order; ``free_order`` lists every block id once.
+    """
+
+    def __init__(self, cfg: SchedConfig, free_order, requests):
+        if cfg.policy not in POLICIES:
+            raise ValueError(f"unknown policy {cfg.policy!r}")
+        self.cfg = cfg
+        order = [int(b) for b in free_order]
+        if sorted(order) != list(range(cfg.num_blocks)):
+            raise ValueError("free_order must list every block id once")
+        self.free = order[::-1]               # a stack: free[-1] is taken next
+        self.ref = [0] * cfg.num_blocks
+        self.reqs = []
+        for i, (p, outs, arr) in enumerate(requests):
+            r = _Request(i, p, outs, arr)
+            if r.prompt < 1 or r.n < 1 or min(r.outs) < 1:
+                raise ValueError(f"request {i}: empty prompt or output")
+            if r.prompt + max(r.outs) - 1 > cfg.max_len:
+                raise ValueError(f"request {i} exceeds max_len")
+            worst = r.n * _cdiv(cfg.max_len if cfg.policy != "paged"
+                                else r.prompt + max(r.outs) - 1, cfg.block_size)
+            if worst > cfg.num_blocks or r.n > cfg.max_seqs:
+                raise ValueError(f"request {i} can never fit")
+            self.reqs.append(r)
+        self.pending = deque(range(len(self.reqs)))
+        self.waiting = deque()
+        self.running = []          # admission order
+        self.slots_used = 0
+        self.pending_copies = []   # prompt copies into reservations, for the next iteration
+        self.it = 0
+
+    # -- block manager ---------------------------------------------------------------
+    def _alloc(self):
+        b = self.free.pop()
+        assert self.ref[b] == 0
+        self.ref[b] = 1
+        return b
+
+    def _release_table(self, table):
+        for b in table:
+            self.ref[b] -= 1
+            assert self.ref[b] >= 0
+            if self.ref[b] == 0:
+                self.free.append(b)
+
+    def _write_slot(self, table, pos, copies):
+        """Slot of logical position ``pos``; allocates on fill, copies a shared block."""
+        bs = self.cfg.block_size
+        j = pos // bs
+        if j == len(table):
+            table.append(self._alloc())
+        elif self.ref[table[j]] > 1:
+            new = self._alloc()
+            copies.append((table[j], new))
+            self.ref[table[j]] -= 1
+            table[j] = new
+        return table[j] * bs + pos % bs
+
+    # -- eviction ----------------------------------------------------------------------
+    def _evict(self, rid, plan):
+        r = self.reqs[rid]
+        if r.state == "prefill":
+            self._release_table(r.table)
+            for t in r.reserved:
+                self._release_table(t)
+            self.slots_used -= r.n
+        else:
+            for s in r.samples:
+                if not s.released:
+                    self._release_table(s.table)
+                    self.slots_used -= 1
+        r.reset()
+        r.evictions += 1
+        self.running.remove(rid)
+        self.waiting.appendleft(rid)
+        plan.preempted.append(rid)
+
+    def _need(self, budget):
+        """Blocks the running requests may take this iteration (an upper bound)."""
+        cfg, n, b = self.cfg, 0, budget
+        for _, _, s in self._decode_samples():
+            if b == 0:
+                break
+            b -= 1
+            if s.ntok % cfg.block_size == 0 or self.ref[s.table[-1]] > 1:
+                n += 1
+        for rid in self.running:
+            r = self.reqs[rid]
+            if r.state == "prefill":
+                L = min(r.prompt - r.prefilled, cfg.max_chunk, b)
+                if L <= 0:
+                    break
+                n += _cdiv(r.prefilled + L, cfg.block_size) - len(r.table)
+                b -= L
+        return n
+
+    def _decode_samples(self):
+        for rid in self.running:
+            r = self.reqs[rid]
+            if r.state == "decode":
+                for k, s in enumerate(r.samples):
+                    if not s.done:
+                        yield rid, k, s
+
+    # -- prefill -----------------------------------------------------------------------
+    def _chunk(self, rid, plan, budget, pre_slots):
+        """Schedule the next prefill chunk of ``rid`` (its blocks are available); its length."""
+        cfg, r = self.cfg, self.reqs[rid]
+        L = min(r.prompt - r.prefilled, cfg.max_chunk, budget)
+        if L <= 0:
+            return 0
+        q_start = len(pre_slots)
+        for pos in range(r.prefilled, r.prefilled + L):
+            pre_slots.append(self._write_slot(r.table, pos, plan.copies))
+        r.prefilled += L
+        plan.chunks.append((rid, q_start, L, r.prefilled, list(r.table)))
+        if r.prefilled == r.prompt:          # the prompt's last chunk: fork into samples
+            r.state = "decode"
+            r.samples = [_Sample(r.table, r.prompt, r.outs[0])]
+            for k in range(1, r.n):
+                if cfg.policy == "paged":
+                    for b in r.table:
+                        self.ref[b] += 1
+                    t = list(r.table)
+                else:
+                    t = r.reserved[k - 1]
+                    for j in range(_cdiv(r.prompt, cfg.block_size)):
+                        self.pending_copies.append((r.table[j], t[j]))
+                r.samples.append(_Sample(t, r.prompt, r.outs[k]))
+            r.reserved = []
+            plan.generated += r.n
+        return L
+
+    # -- one iteration ---------------------------------------------------------------
+    def done(self):
+        return not self.pending and not self.waiting and not self.running
+
+    def step(self):
+        """Plan and apply one iteration; None once every request has finished."""
+        if self.done():
+            return None
+        cfg = self.cfg
+        plan = Plan(self.it)
+        plan.copies.extend(self.pending_copies)
+        self.pending_copies = []
+        while self.pending and self.reqs[self.pending[0]].arrival <= self.it:
+            self.waiting.append(self.pending.popleft())
+        batch_empty = not self.running
+        budget = cfg.max_tokens
+        # eviction until the running requests' appends of this iteration fit
+        if cfg.policy == "paged":
+            while self._need(budget) > len(self.free):
+                if len(self.running) <= 1:
+                    raise AssertionError("a lone request does not fit the pool")
+                self._evict(self.running[-1], plan)
+        dec_slots = []
+        for rid, k, s in list(self._decode_samples()):
+            if budget == 0:
+                break
+            dec_slots.append(self._write_slot(s.table, s.ntok, plan.copies))
+            s.ntok += 1
+            s.gen += 1
+            s.done = s.gen == s.out
+            plan.decodes.append((rid, k, s.ntok, list(s.table)))
+            plan.generated += 1
+            budget -= 1
+        pre_slots = []
+        for rid in list(self.running):
+            if self.reqs[rid].state == "prefill":
+                budget -= self._chunk(rid, plan, budget, pre_slots)
+        admitting = not plan.preempted and (cfg.policy != "static" or batch_empty)
+        while admitting and self.waiting and budget > 0:
+            rid = self.waiting[0]
+            r = self.reqs[rid]
+            if self.slots_used + r.n > cfg.max_seqs:
+                break
+            if cfg.policy == "paged":
+                first = min(r.prompt, cfg.max_chunk, budget)
+                if _cdiv(first, cfg.block_size) > len(self.free):
+                    break
+            else:
+                R = _cdiv(cfg.max_len, cfg.block_size)
+                if r.n * R > len(self.free):
+                    break
+                r.table = [self._alloc() for _ in range(R)]
+                r.reserved = [[self._alloc() for _ in range(R)] for _ in range(r.n - 1)]
+            self.waiting.popleft()
+            self.running.append(rid)
+            self.slots_used += r.n
+            r.state = "prefill"
+            plan.admitted.append(rid)
+            budget -= self._chunk(rid, plan, budget, pre_slots)
+        plan.slots = pre_slots + dec_slots
+        # release what finished in this iteration (after its kernels have run)
+        if cfg.policy == "static":
+            if self.running and all(self.reqs[rid].state == "decode" and
+                                    all(s.done for s in self.reqs[rid].samples)
+                                    for rid in self.running):
+                for rid in self.running:
+                    for s in self.reqs[rid].samples:
+                        self._release_table(s.table)
+                    self.reqs[rid].state = "done"
+                    plan.finished.append(rid)
+                self.running = []
+                self.slots_used = 0
+        else:
+            for rid in list(self.running):
+                r = self.reqs[rid]
+                if r.state != "decode":
+                    continue
+                for s in r.samples:
+                    if s.done and not s.released:
+                        self._release_table(s.table)
+                        s.released = True
+                        self.slots_used -= 1
+                if all(s.released for s in r.samples):
+                    r.state = "done"
+                    self.running.remove(rid)
+                    plan.finished.append(rid)
+        self.it += 1
+        if not (plan.slots or plan.copies or plan.preempted or plan.finished) and not self.pending:
+            # nothing ran and nothing is yet to arrive: with the pool whole and
+            # every request fitting alone, this cannot happen
+            raise AssertionError(f"iteration {plan.iteration} made no progress")
+        return plan
+
+    def run(self):
+        """Every plan until all requests finish."""
+        plans = []
+        while (p := self.step()) is not None:
+            plans.append(p)
+        return plans

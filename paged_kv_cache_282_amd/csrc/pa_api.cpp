@@ -2,6 +2,7 @@
 // contract of every entry point. Nothing here allocates, synchronises or reads
 // device memory; every check runs on the host before anything is enqueued.
 #include "pa.h"
+#include "pa_sched.h"
 
 #include <hip/hip_runtime.h>
 
@@ -158,6 +159,8 @@ const char* pa_status_string(int status) {
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_ALIAS: return "output overlaps an input";
     case PA_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
+    case PA_SCHED_FINISHED: return "every request has finished";
+    case PA_ERR_STATE: return "scheduler invariant broken (a lone request does not fit, or no progress)";
     default: return "unknown status";
   }
 }

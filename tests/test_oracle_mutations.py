@@ -35,13 +35,31 @@ MUTATIONS = {
                               "l = sum(p[1] for p in finite)"),
 }
 
+# name -> (text in oracle/scheduler.py, replacement); caught by test_sched_oracle.py
+SCHED_MUTATIONS = {
+    "copy_on_write_skipped": ("elif self.ref[table[j]] > 1:", "elif False:"),
+    "free_list_first_in_first_out": ("b = self.free.pop()", "b = self.free.pop(0)"),
+    "evicts_the_oldest": ("self._evict(self.running[-1], plan)",
+                          "self._evict(self.running[0], plan)"),
+    "finished_blocks_kept": ("self._release_table(s.table)\n                        s.released",
+                             "s.released"),
+    "static_batch_ends_at_first_finish": ("if self.running and all(self.reqs[rid].state",
+                                          "if self.running and any(self.reqs[rid].state"),
+    "chunk_overruns_budget": ("L = min(r.prompt - r.prefilled, cfg.max_chunk, budget)\n        if",
+                              "L = min(r.prompt - r.prefilled, cfg.max_chunk, budget + 1)\n        if"),
+    "fork_without_reference": ("                    for b in r.table:\n                        self.ref[b] += 1\n",
+                               ""),
+    "prefill_token_not_counted": ("self.gen = 1 ", "self.gen = 0 "),
+}
+
 
 def _copy_tree(dst):
     for d in ("oracle", "workloads"):
         shutil.copytree(os.path.join(ROOT, d), os.path.join(dst, d),
                         ignore=shutil.ignore_patterns("__pycache__"))
     os.makedirs(os.path.join(dst, "tests"))
-    for f in ("__init__.py", "conftest.py", "pool_writer.py", "test_oracle_pins.py"):
+    for f in ("__init__.py", "conftest.py", "pool_writer.py", "test_oracle_pins.py",
+              "test_sched_oracle.py"):
         src = os.path.join(ROOT, "tests", f)
         if os.path.exists(src):
             shutil.copy(src, os.path.join(dst, "tests", f))
@@ -61,5 +79,22 @@ def test_planted_mistake_is_caught(name, tmp_path):
     env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_pins.py", "-x", "-q",
                         "-p", "no:cacheprovider", "-m", "not gpu"],
+                       cwd=str(tmp_path), capture_output=True, text=True, env=env, timeout=600)
+    assert r.returncode == 1, f"planted mistake {name} was not caught:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(SCHED_MUTATIONS))
+def test_planted_scheduler_mistake_is_caught(name, tmp_path):
+    old, new = SCHED_MUTATIONS[name]
+    _copy_tree(str(tmp_path))
+    path = os.path.join(str(tmp_path), "oracle", "scheduler.py")
+    with open(path) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"the oracle no longer contains the text {name} mutates"
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_sched_oracle.py", "-x", "-q",
+                        "-p", "no:cacheprovider", "-m", "not gpu", "--timeout", "120"],
                        cwd=str(tmp_path), capture_output=True, text=True, env=env, timeout=600)
     assert r.returncode == 1, f"planted mistake {name} was not caught:\n{r.stdout[-2000:]}"
