@@ -24,6 +24,10 @@ Reported (one JSON line on stdout):
              bytes or flops, fraction of the matching roofline, and the oracle's
              rate on a bounded sample of the same inputs
   cpu_baseline  the fp64 NumPy oracle on one full headline layer, 1 thread
+  engine     the C++ block manager + iteration-level scheduler driving these
+             kernels on a long-tail request stream, under paged allocation,
+             Orca-style max-length reservation and static batching: output
+             tokens/s, host time per iteration, decode KV GB/s of the loop
 """
 from __future__ import annotations
 
@@ -353,6 +357,99 @@ class Rows:
         return self.out
 
 
+ENGINE_DESC = ("iteration-level serving loop (no model weights): 1024 requests arriving at "
+               "once, prompts U[32, 512], outputs round(lognormal(median 128, sigma 1)) "
+               "clipped [1, 1536], 20% of requests with 4 parallel samples; 32 q / 8 kv heads, "
+               "head_dim 128, block_size 16, bf16; pool 8192 blocks (512 MB); at most 256 "
+               "running samples, 2048 tokens and 512-token prefill chunks per iteration, "
+               "max_len 2048 (reservation: 128 blocks per sample)")
+
+
+def engine_rows(pa, torch, oracle_on: bool) -> dict:
+    """The C++ engine loop under the three policies on one request stream.
+
+    tokens/s counts each request's output tokens once (work lost to eviction
+    is not counted); wall time runs from the first iteration to the final
+    stream synchronisation, host scheduling and kernel time together. The
+    host's own time (planning, packing, enqueueing) is reported apart from
+    the time it waits for the device to free a ring slot.
+    """
+    from paged_kv_cache_282_amd import runtime
+    from workloads.requests import make_request_stream
+
+    cfg = dict(num_blocks=8192, block_size=16, max_seqs=256, max_tokens=2048, max_chunk=512,
+               max_len=2048)
+    HQ, HKV, D = 32, 8, 128
+    reqs = make_request_stream(282, 1024, prompt=(32, 512), multi_frac=0.2, samples=4,
+                               output_lognormal=(128, 1.0, 1536))
+    order = np.random.default_rng(282).permutation(cfg["num_blocks"])
+    T, S = cfg["max_tokens"], cfg["max_seqs"]
+    g = torch.Generator(device="cuda").manual_seed(282)
+    pool = torch.randn(cfg["num_blocks"] * 2 * HKV * cfg["block_size"] * D, generator=g,
+                       device="cuda").bfloat16()
+    k, v = (torch.randn(T, HKV, D, generator=g, device="cuda").bfloat16() for _ in range(2))
+    qp = torch.randn(T, HQ, D, generator=g, device="cuda").bfloat16()
+    qd = torch.randn(S, HQ, D, generator=g, device="cuda").bfloat16()
+    outp, outd = torch.empty_like(qp), torch.empty_like(qd)
+    scale = 1.0 / np.sqrt(D)
+    want = sum(sum(o) for _, o, _ in reqs)
+
+    def run(policy, stream_reqs):
+        ws = pa.new_decode_workspace(S, HQ, D, cfg["max_len"])
+        sched = runtime.Scheduler(policy=policy, free_order=order, requests=stream_reqs, **cfg)
+        eng = runtime.Engine(sched, pool, HKV, qp, qd, k, v, outp, outd, ws, scale)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        st = eng.run()
+        wall = time.perf_counter() - t0
+        eng.close()
+        sched.close()
+        return st, wall
+
+    run("paged", reqs[:64])   # first launches of every kernel, outside the timed runs
+    out = {"workload": ENGINE_DESC, "output_tokens": want, "policies": {}}
+    for policy in ("paged", "reserve", "static"):
+        st, wall = run(policy, reqs)
+        kv = st["decode_context_tokens"] * 2 * HKV * D * 2
+        it = st["iterations"]
+        out["policies"][policy] = {
+            "tokens_per_s": round(want / wall, 1), "wall_ms": round(wall * 1e3, 2),
+            "iterations": it, "us_per_iteration": round(wall * 1e6 / it, 2),
+            "host_us_per_iteration": round(st["host_us"] / it, 2),
+            "host_fraction": round(st["host_us"] * 1e-6 / wall, 4),
+            "host_wait_fraction": round(st["wait_us"] * 1e-6 / wall, 4),
+            "mean_decodes_per_iteration": round(st["decode_tokens"] / it, 1),
+            "generated": st["generated"], "evictions": st["evictions"],
+            "copies": st["copies"], "prefill_tokens": st["prefill_tokens"],
+            "decode_kv_GBps": round(kv / wall / 1e9, 1),
+            "decode_kv_frac_of_hbm_peak": round(kv / wall / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"  engine {policy:8s} {want / wall:10.0f} tok/s  {it:6d} iterations  "
+            f"{wall * 1e3:8.1f} ms  host {st['host_us'] / it:6.1f} us/iter  "
+            f"decode KV {kv / wall / 1e9:7.1f} GB/s  evictions {st['evictions']}")
+    pol = out["policies"]
+    out["paged_vs_static"] = round(pol["paged"]["tokens_per_s"] / pol["static"]["tokens_per_s"], 2)
+    out["reserve_vs_static"] = round(pol["reserve"]["tokens_per_s"]
+                                     / pol["static"]["tokens_per_s"], 2)
+    if oracle_on:
+        from oracle.scheduler import SchedConfig, Scheduler
+        t0 = time.perf_counter()
+        plans = Scheduler(SchedConfig(policy="paged", **cfg), order, reqs).run()
+        dt = time.perf_counter() - t0
+        agree = (len(plans) == pol["paged"]["iterations"] and
+                 sum(p.generated for p in plans) == pol["paged"]["generated"] and
+                 sum(len(p.preempted) for p in plans) == pol["paged"]["evictions"])
+        out["cpu_oracle"] = {"value": round(len(plans) / dt, 1), "unit": "iterations/s",
+                             "cores": 1, "kind": "oracle",
+                             "sample": "the paged policy's whole schedule (plans only, no "
+                                       "attention), pure Python",
+                             "seconds": round(dt, 2), "native_plan_totals_agree": agree,
+                             "native_host_iterations_per_s": round(
+                                 1e6 / pol["paged"]["host_us_per_iteration"], 1)}
+        log(f"  oracle scheduler: {len(plans)} iterations in {dt:.1f} s, totals agree: {agree}")
+    del pool
+    return out
+
+
 def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -496,6 +593,9 @@ def main() -> int:
         log("rows:")
         result["rows"] = Rows(pa, torch, args.repeats, not args.no_cpu_baseline).run(
             make_workload)
+        torch.cuda.empty_cache()
+        log("engine loop:")
+        result["engine"] = engine_rows(pa, torch, not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -119,9 +119,11 @@ int32_t pa_sched_num_free(const pa_sched* s);
  *   6. Admission (not after an eviction; STATIC only when no batch was
  *      running at the start of the iteration): the head of the queue is
  *      admitted while it fits the free slots (its samples count from
- *      admission on), the budget, and the pool (PAGED: the blocks of its first
- *      chunk; reservation policies: ceil(max_len/bs) blocks per sample,
- *      taken now), and gets its first chunk. The chunk that completes a
+ *      admission on), the budget (continuous policies only: a static batch is
+ *      formed whole and its later members start prefill in later iterations),
+ *      and the pool (PAGED: the blocks of its first chunk; reservation
+ *      policies: ceil(max_len/bs) blocks per sample, taken now), and gets its
+ *      first chunk if budget is left. The chunk that completes a
  *      prompt produces every sample's first token; PAGED samples then share
  *      the prompt's blocks.
  *   7. Samples that produced their last token release their blocks and slot
@@ -175,9 +177,11 @@ typedef struct {
   int64_t generated;      /* tokens produced, including those of evicted attempts */
   int64_t prefill_tokens; /* prompt tokens processed, including recomputation */
   int64_t decode_tokens;
+  int64_t decode_context_tokens; /* sum of the decodes' context lengths (tokens attended) */
   int64_t copies;
   int64_t evictions;
   double host_us;         /* host time spent planning and enqueueing */
+  double wait_us;         /* host time spent waiting for a ring slot (the device is behind) */
 } pa_engine_stats;
 
 int pa_engine_create(pa_sched* s, void* kv_pool, int32_t num_kv_heads, int32_t num_q_heads,

@@ -31,6 +31,9 @@ the design notes):
     requests before admitting new ones;
   * admission is first come, first served and never skips the head of the
     queue; a request with n samples takes n batch slots from admission on;
+    continuous batching admits only while the iteration's token budget lasts,
+    while a static batch is formed whole (its later members start their
+    prefill in the following iterations);
   * a decode sequence appends the KV of its previous token and produces the
     next; a prompt's last prefill chunk produces every sample's first token;
   * the free list is a stack: blocks are taken in ``free_order`` at first and
@@ -289,7 +292,9 @@ class Scheduler:
             if self.reqs[rid].state == "prefill":
                 budget -= self._chunk(rid, plan, budget, pre_slots)
         admitting = not plan.preempted and (cfg.policy != "static" or batch_empty)
-        while admitting and self.waiting and budget > 0:
+        # a static batch is formed whole; continuous batching admits only what
+        # this iteration's budget can start on
+        while admitting and self.waiting and (budget > 0 or cfg.policy == "static"):
             rid = self.waiting[0]
             r = self.reqs[rid]
             if self.slots_used + r.n > cfg.max_seqs:

@@ -330,7 +330,10 @@ struct pa_sched {
       if (reqs[rid].phase == Phase::kPrefill) budget -= prefill_chunk(rid, budget);
     const bool may_admit =
         plan.preempted.empty() && (cfg.policy != PA_POLICY_STATIC || batch_open);
-    while (may_admit && !queue.empty() && budget > 0 && admit_head(budget))
+    // A static batch is formed whole; continuous batching admits only what the
+    // budget can start on this iteration.
+    const bool whole_batch = cfg.policy == PA_POLICY_STATIC;
+    while (may_admit && !queue.empty() && (budget > 0 || whole_batch) && admit_head(budget))
       budget -= prefill_chunk(running.back(), budget);
     release_finished();
     ++iteration;
@@ -462,13 +465,16 @@ struct pa_engine {
   }
 
   int step(int32_t* out, int64_t out_cap, int64_t* used_words) {
-    const auto t0 = std::chrono::steady_clock::now();
+    using clock = std::chrono::steady_clock;
+    const auto t0 = clock::now();
     if (out && out_cap < s->capacity()) return PA_ERR_SHAPE;
     const int st = s->step();
     if (st != PA_OK) return st;
     const int slot = next;
     next = (next + 1) % kRing;
+    const auto t1 = clock::now();
     if (used[slot] && hipEventSynchronize(sent[slot]) != hipSuccess) return PA_ERR_LAUNCH;
+    const auto t2 = clock::now();
     int32_t* h = host_ring + slot * cap;
     int32_t* dv = dev_ring + slot * cap;
     s->write(h);
@@ -485,10 +491,13 @@ struct pa_engine {
     stats.generated += h[1];
     stats.prefill_tokens += h[4];
     stats.decode_tokens += h[6];
+    for (int32_t ctx : s->plan.dec_ctx) stats.decode_context_tokens += ctx;
     stats.copies += h[2];
     stats.evictions += h[8];
-    stats.host_us +=
-        std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+    const auto t3 = clock::now();
+    using us = std::chrono::duration<double, std::micro>;
+    stats.host_us += us(t1 - t0).count() + us(t3 - t2).count();
+    stats.wait_us += us(t2 - t1).count();
     return ls;
   }
 };

@@ -28,8 +28,9 @@ class _Config(ctypes.Structure):
 
 class EngineStats(ctypes.Structure):
     _fields_ = [("iterations", _i64), ("generated", _i64), ("prefill_tokens", _i64),
-                ("decode_tokens", _i64), ("copies", _i64), ("evictions", _i64),
-                ("host_us", ctypes.c_double)]
+                ("decode_tokens", _i64), ("decode_context_tokens", _i64), ("copies", _i64),
+                ("evictions", _i64),
+                ("host_us", ctypes.c_double), ("wait_us", ctypes.c_double)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -1,0 +1,143 @@
+"""The engine loop (libpa's C++ scheduler driving its HIP kernels) against the
+oracle, iteration by iteration, on the GPU.
+
+Every iteration: the native plan must equal the scheduler oracle's plan; the
+pool after the iteration's copies and appends must equal, bit for bit, the
+oracle's copy_blocks then append applied to the oracle's own pool; and every
+decode and prefill output must match the attention oracle on that pool within
+the dtype's bound. The pool starts NaN-filled, so a read of any slot that was
+never written shows up in the outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_282_amd as pa
+from oracle.scheduler import SchedConfig, Scheduler as OracleScheduler
+from paged_kv_cache_282_amd import runtime
+from tests.gpu_helpers import TOL, bits, to_dev, values
+from workloads.requests import make_request_stream
+from workloads.rng import normal_values
+
+HKV, HQ, D, BS = 2, 4, 64, 16
+
+
+def _raw_bits(a):
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def _padded(t, mb):
+    return list(t) + [0] * (mb - len(t))
+
+
+def _nan_pool(nb, dtype):
+    n = nb * 2 * HKV * BS * D
+    if dtype == "bf16":
+        return np.full(n, 0x7FC0, np.uint16).reshape(nb, -1)
+    return np.full(n, np.nan, np.float32).reshape(nb, -1)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("policy,dtype", [("paged", "bf16"), ("paged", "f32"),
+                                          ("reserve", "bf16"), ("static", "f32")])
+def test_engine_matches_the_oracle_every_iteration(policy, dtype):
+    print(f"\nengine parity: policy={policy} dtype={dtype}", flush=True)
+    # 20 blocks of 16 tokens: tight enough that the paged policy evicts
+    cfg = dict(num_blocks=20, block_size=BS, max_seqs=6, max_tokens=48, max_chunk=32,
+               max_len=128)
+    reqs = make_request_stream(21, 14, prompt=(1, 70), output=(1, 40), multi_frac=0.3,
+                               samples=2, arrival_every=2)
+    order = np.random.default_rng(2).permutation(cfg["num_blocks"])
+    mb = -(-cfg["max_len"] // BS)
+    scale = 1.0 / np.sqrt(D)
+    ss = np.random.SeedSequence(77).spawn(4)
+    T, S = cfg["max_tokens"], cfg["max_seqs"]
+    k_raw = normal_values(ss[0], T * HKV * D, dtype).reshape(T, HKV, D)
+    v_raw = normal_values(ss[1], T * HKV * D, dtype).reshape(T, HKV, D)
+    qp_raw = normal_values(ss[2], T * HQ * D, dtype).reshape(T, HQ, D)
+    qd_raw = normal_values(ss[3], S * HQ * D, dtype).reshape(S, HQ, D)
+    ref = _nan_pool(cfg["num_blocks"], dtype)
+
+    pool = to_dev(ref, dtype)
+    k, v, qp, qd = (to_dev(a, dtype) for a in (k_raw, v_raw, qp_raw, qd_raw))
+    outp, outd = torch.zeros_like(qp), torch.zeros_like(qd)
+    ws = pa.new_decode_workspace(S, HQ, D, cfg["max_len"])
+    sched = runtime.Scheduler(policy=policy, free_order=order, requests=reqs, **cfg)
+    eng = runtime.Engine(sched, pool, HKV, qp, qd, k, v, outp, outd, ws, scale)
+    osched = OracleScheduler(SchedConfig(policy=policy, **cfg), order, reqs)
+    n_dec = n_pre = n_copies = n_evict = 0
+    while True:
+        got = eng.step()
+        want = osched.step()
+        if got is None:
+            assert want is None
+            break
+        it = want.iteration
+        assert got["copies"] == [tuple(c) for c in want.copies], it
+        assert got["slots"] == want.slots, it
+        assert [tuple(c) for c in got["chunks"]] == \
+            [(r, q0, L, ctx, _padded(t, mb)) for r, q0, L, ctx, t in want.chunks], it
+        assert [tuple(x) for x in got["decodes"]] == \
+            [(r, s, ctx, _padded(t, mb)) for r, s, ctx, t in want.decodes], it
+        torch.cuda.synchronize()
+        # the oracle's own pool after this iteration's copies and appends
+        if want.copies:
+            ref = oracle.copy_blocks(ref, np.asarray(want.copies, np.int64))
+        nt = len(want.slots)
+        if nt:
+            ref = oracle.append(ref, k_raw[:nt], v_raw[:nt], np.asarray(want.slots), HKV, BS, D)
+        assert np.array_equal(_raw_bits(bits(pool)), _raw_bits(ref)), f"pool, iteration {it}"
+        if want.decodes:
+            nd = len(want.decodes)
+            tabs = np.array([_padded(t, mb) for *_, t in want.decodes], np.int64)
+            ctx = np.array([c for _, _, c, _ in want.decodes], np.int64)
+            exp = oracle.decode(qd_raw[:nd], ref, tabs, ctx, HKV, BS, scale, dtype)
+            err = np.abs(values(outd[:nd]) - exp).max()
+            assert err <= TOL[dtype], f"decode, iteration {it}: {err}"
+            n_dec += nd
+        if want.chunks:
+            npre = sum(c[2] for c in want.chunks)
+            tabs = np.array([_padded(t, mb) for *_, t in want.chunks], np.int64)
+            ctx = np.array([c[3] for c in want.chunks], np.int64)
+            qsl = np.array([c[1] for c in want.chunks] + [npre], np.int64)
+            exp = oracle.prefill(qp_raw[:npre], ref, tabs, ctx, qsl, HKV, BS, scale, dtype)
+            err = np.abs(values(outp[:npre]) - exp).max()
+            assert err <= TOL[dtype], f"prefill, iteration {it}: {err}"
+            n_pre += npre
+        n_copies += len(want.copies)
+        n_evict += len(want.preempted)
+    eng.close()
+    assert sched.num_free() == cfg["num_blocks"]
+    assert n_dec > 0 and n_pre > 0 and n_copies > 0
+    assert n_evict > 0 or policy != "paged"
+    print(f"  {osched.it} iterations, {n_pre} prefill tokens, {n_dec} decodes, "
+          f"{n_copies} copies", flush=True)
+
+
+@pytest.mark.gpu
+def test_engine_run_counts_every_token():
+    cfg = dict(num_blocks=64, block_size=BS, max_seqs=8, max_tokens=64, max_chunk=32,
+               max_len=128)
+    reqs = make_request_stream(5, 30, prompt=(1, 60), output=(1, 60), multi_frac=0.3,
+                               samples=3)
+    order = np.random.default_rng(3).permutation(cfg["num_blocks"])
+    T, S = cfg["max_tokens"], cfg["max_seqs"]
+    pool = torch.zeros(cfg["num_blocks"] * 2 * HKV * BS * D, dtype=torch.bfloat16, device="cuda")
+    k = torch.randn(T, HKV, D, device="cuda").bfloat16()
+    v = torch.randn(T, HKV, D, device="cuda").bfloat16()
+    qp = torch.randn(T, HQ, D, device="cuda").bfloat16()
+    qd = torch.randn(S, HQ, D, device="cuda").bfloat16()
+    outp, outd = torch.zeros_like(qp), torch.zeros_like(qd)
+    ws = pa.new_decode_workspace(S, HQ, D, cfg["max_len"])
+    sched = runtime.Scheduler(policy="paged", free_order=order, requests=reqs, **cfg)
+    eng = runtime.Engine(sched, pool, HKV, qp, qd, k, v, outp, outd, ws, 0.125)
+    stats = eng.run()
+    plans = OracleScheduler(SchedConfig(policy="paged", **cfg), order, reqs).run()
+    assert stats["iterations"] == len(plans)
+    assert stats["generated"] == sum(p.generated for p in plans)
+    assert stats["evictions"] == sum(len(p.preempted) for p in plans)
+    assert stats["copies"] == sum(len(p.copies) for p in plans)
+    assert sched.num_free() == cfg["num_blocks"]
+    assert torch.isfinite(outd.float()).all()
+    eng.close()
