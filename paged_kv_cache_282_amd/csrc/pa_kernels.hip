@@ -1056,23 +1056,24 @@ struct PrefillSmem {
   uint16_t v[2][(kStep / 4) * D * 4];        // [4-token slice][dim][4]
 };
 
+// One workgroup tile: positions x*kWaves*pos_per_wave .. of chunk c, kv head g.
+// Every branch that returns early is uniform over the workgroup, and every
+// path that reaches the step loop runs the same barriers in every wave.
 template <int D, int BS, int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_bf16_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D>& sm, int x,
+                                             int c, int g) {
   using Eng = Bf16Engine<D, BS, NT>;
   constexpr int KS = Eng::KS, VT = Eng::VT;
   constexpr int kChunks = 2 * D * kStep * 2 / 16;  // 16-byte pieces of one step's K and V
   constexpr int kPer = kChunks / 256;              // per thread
   static_assert(kChunks % 256 == 0, "a step is a whole number of 16-byte pieces per thread");
-  __shared__ PrefillSmem<D> sm;
-  const int c = blockIdx.y, g = blockIdx.z;
   int q0, L, prior;
   if (!chunk_geometry(a, c, a.mb * BS, q0, L, prior)) return;  // uniform per workgroup
   const int G = a.hq / a.hkv;
   const int pos_per_wave = 16 * NT / G;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wg_i0 = blockIdx.x * kWaves * pos_per_wave;
+  const int wg_i0 = x * kWaves * pos_per_wave;
   if (wg_i0 >= L) return;  // uniform per workgroup
   const int i0 = wg_i0 + wave * pos_per_wave;
   const int r = lane & 15, kg = lane >> 4;
@@ -1183,6 +1184,61 @@ void prefill_bf16_kernel(PrefillArgs a) {
              (static_cast<uint32_t>(f32_to_bf16_bits(eng.o[nt][j][3] * inv)) << 16);
       *reinterpret_cast<u32x2*>(orow + 16 * j + 4 * kg) = w;
     }
+  }
+}
+
+// One workgroup per tile, in grid order: (x, chunk, kv head) = blockIdx.
+template <int D, int BS, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_bf16_kernel(PrefillArgs a) {
+  __shared__ PrefillSmem<D> sm;
+  prefill_tile<D, BS, NT>(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Tiles in longest-first order. A tile's work is its number of 32-token key
+// steps, known from the chunk geometry alone, so every workgroup ranks the
+// (chunk, x) tiles by it in LDS (ties: lower index first; the kv heads of one
+// (chunk, x) follow each other). Round k hands tile k*P + w (k even) or
+// k*P + P-1-w (k odd) to workgroup w: a serpentine deal of the sorted list,
+// which keeps the longest tiles from ending up on the same workgroups.
+constexpr int kMaxPrefillTiles = 1024;  // (chunk, x) pairs ranked in LDS
+
+template <int D, int BS, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_bf16_lpt_kernel(PrefillArgs a, int gx) {
+  __shared__ PrefillSmem<D> sm;
+  __shared__ int s_key[kMaxPrefillTiles];
+  __shared__ int s_order[kMaxPrefillTiles];
+  const int M = a.num_chunks * gx;
+  const int G = a.hq / a.hkv;
+  const int pos_per_wg = kWaves * 16 * NT / G;
+  for (int i = threadIdx.x; i < M; i += kWaves * 64) {
+    const int c = i / gx, x = i - c * gx;
+    int q0, L, prior, key = 0;
+    if (chunk_geometry(a, c, a.mb * BS, q0, L, prior) && x * pos_per_wg < L)
+      key = (prior + min(L, (x + 1) * pos_per_wg) + kStep - 1) / kStep;
+    s_key[i] = key;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < M; i += kWaves * 64) {
+    const int ki = s_key[i];
+    int rank = 0;
+    for (int j = 0; j < M; ++j) {
+      const int kj = s_key[j];
+      rank += (kj > ki || (kj == ki && j < i)) ? 1 : 0;
+    }
+    s_order[rank] = i;
+  }
+  __syncthreads();
+  const int tiles = M * a.hkv;
+  const int P = static_cast<int>(gridDim.x);
+  for (int k = 0; k * P < tiles; ++k) {
+    const int t = k * P + ((k & 1) ? P - 1 - static_cast<int>(blockIdx.x)
+                                   : static_cast<int>(blockIdx.x));
+    if (t >= tiles) break;
+    const int combo = s_order[t / a.hkv];
+    if (s_key[combo] == 0) break;  // sorted: every later tile is empty too
+    prefill_tile<D, BS, NT>(a, sm, combo % gx, combo / gx, t % a.hkv);
   }
 }
 
@@ -1379,8 +1435,19 @@ template <int D, int BS>
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int max_chunk_len, hipStream_t st) {
   const int G = a.hq / a.hkv;
   const int pos_per_wg = kWaves * 16 * kPrefillNT / G;
-  dim3 grid((max_chunk_len + pos_per_wg - 1) / pos_per_wg, a.num_chunks, a.hkv);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, BS, kPrefillNT>), grid, dim3(256), 0, st, a);
+  const int gx = (max_chunk_len + pos_per_wg - 1) / pos_per_wg;
+  const int64_t combos = static_cast<int64_t>(gx) * a.num_chunks;
+  if (combos <= kMaxPrefillTiles) {
+    static const int resident = resident_workgroups(prefill_bf16_lpt_kernel<D, BS, kPrefillNT>);
+    const int64_t tiles = combos * a.hkv;
+    const int64_t cap = resident > 0 ? resident : 512;
+    const int w = static_cast<int>(tiles < cap ? tiles : cap);
+    hipLaunchKernelGGL((prefill_bf16_lpt_kernel<D, BS, kPrefillNT>), dim3(w), dim3(256), 0, st,
+                       a, gx);
+  } else {
+    dim3 grid(gx, a.num_chunks, a.hkv);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, BS, kPrefillNT>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

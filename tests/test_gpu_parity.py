@@ -112,6 +112,28 @@ def test_prefill_ragged_chunks():
     _check_step(w, "prefill-ragged")
 
 
+def test_prefill_with_many_tiles():
+    """33 chunks whose longest is 512 queries: at G = 8 that is 33 x 32 (chunk,
+    position-block) tiles, more than the longest-first kernel ranks in LDS, so
+    the one-workgroup-per-tile kernel runs; the other chunks are short."""
+    w = make_workload("mixed", seed=4242, num_decode=1, num_chunks=33, chunk_len=512,
+                      max_prior=64, num_q_heads=16, num_kv_heads=2, head_dim=64, dec_min=1,
+                      dec_max=100)
+    rng = np.random.default_rng(5)
+    lens = [512] + [int(x) for x in rng.integers(1, 41, 32)]
+    q, qsl, ctx = [], [0], []
+    for c, L in enumerate(lens):
+        lo = int(w.query_start_loc[c])
+        q.append(w.prefill_q[lo:lo + L])
+        qsl.append(qsl[-1] + L)
+        ctx.append(int(w.prefill_context_lens[c]) - 512 + L)
+    w.prefill_q = np.concatenate(q)
+    w.query_start_loc = np.array(qsl, np.int32)
+    w.prefill_context_lens = np.array(ctx, np.int32)
+    assert len(lens) * 512 // 16 > 1024
+    _check_step(w, "prefill-many-tiles")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_single_token_context_returns_v_bit_exactly(dtype):
     w = build_decode_workload("one", 7, [1] * 9, 8, 2, 128, 16, dtype)
