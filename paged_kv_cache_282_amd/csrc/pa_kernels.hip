@@ -143,6 +143,10 @@ __device__ __forceinline__ int clamp_block(int blk, int64_t nb) {
 //     B (P)   lane gives row n at the same eight tokens (its own scores)
 //     C       lane (kg, n) holds O^T[16j + 4kg + i][n], i < 4.
 // ---------------------------------------------------------------------------
+// How far (in base-2 exponent) the running maximum may pass the reference
+// maximum before the softmax state is rescaled; weights stay below 2^8.
+constexpr float kRescaleSlack = 8.f;
+
 template <int D, int BS, int NT>
 struct Bf16Engine {
   static constexpr int KS = D / 32;
@@ -266,8 +270,14 @@ struct Bf16Engine {
       float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                        fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
       mx = max_over_groups(mx);
-      // scaling by sl2e > 0 is monotone, so the scaled maximum is mx * sl2e
-      const float mnew = fmaxf(m[nt], mx * sl2e);
+      // scaling by sl2e > 0 is monotone, so the scaled maximum is mx * sl2e.
+      // The reference m only moves when the running maximum passes it by more
+      // than kRescaleSlack (base 2): until then the weights exp2(s - m) stay
+      // below 2^kRescaleSlack, and the state needs no rescale. Any reference
+      // gives the same softmax, since O and l share it.
+      const float mtop = fmaxf(m[nt], mx * sl2e);
+      const float mnew =
+          (m[nt] == -__builtin_inff() || mtop > m[nt] + kRescaleSlack) ? mtop : m[nt];
       const float muse = (mnew == -__builtin_inff()) ? 0.f : mnew;
       const float alpha = exp2_fast(m[nt] - muse);
       bf16x8 p;
