@@ -221,9 +221,28 @@ struct Bf16Engine {
     }
   }
 
-  // Consume a loaded step starting at token t0. Tokens >= vend have their V
-  // zeroed (they may be NaN); scores of tokens past a row's limit are -inf.
-  __device__ __forceinline__ void compute(KV& kv, int t0, int vend, int lane, float sl2e) {
+  // First half of a step: q.k of every tile, from the K operands alone.
+  __device__ __forceinline__ void scores(const u32x4 (&kA)[KS], const u32x4 (&kB)[KS],
+                                         f32x4 (&sa)[NT], f32x4 (&sb)[NT]) const {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      sa[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sb[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        sa[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kA[s]),
+                                                         qreg[nt][s], sa[nt], 0, 0, 0);
+        sb[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kB[s]),
+                                                         qreg[nt][s], sb[nt], 0, 0, 0);
+      }
+    }
+  }
+
+  // Second half of a step starting at token t0: masks, online softmax and
+  // p.V for every tile. Tokens >= vend have their V zeroed (they may be NaN);
+  // scores of tokens past a row's limit are -inf.
+  __device__ __forceinline__ void finish(f32x4 (&sa)[NT], f32x4 (&sb)[NT], u32x4 (&vv)[VT],
+                                         int t0, int vend, int lane, float sl2e) {
     const int kg = lane >> 4;
     // element e of this lane's eight tokens: e < 4 -> t0 + 4kg + e (set a),
     // e >= 4 -> t0 + 16 + 4kg + e - 4 (set b)
@@ -236,25 +255,17 @@ struct Bf16Engine {
         const int e0 = 2 * (w & 1);
         const uint32_t mask = (e0 < nv ? 0x0000FFFFu : 0u) | (e0 + 1 < nv ? 0xFFFF0000u : 0u);
 #pragma unroll
-        for (int j = 0; j < VT; ++j) kv.vv[j][w] &= mask;
+        for (int j = 0; j < VT; ++j) vv[j][w] &= mask;
       }
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv.kA[s]),
-                                                     qreg[nt][s], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv.kB[s]),
-                                                     qreg[nt][s], sb, 0, 0, 0);
-      }
       // raw scores q.k; the softmax runs in base 2 on q.k * sl2e
       float sc[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sc[i] = sa[i];
-        sc[4 + i] = sb[i];
+        sc[i] = sa[nt][i];
+        sc[4 + i] = sb[nt][i];
       }
       // Mask the scores of tokens past a row's limit. Only steps that reach
       // past the limit of some real row need it (wave-uniform test); then
@@ -300,9 +311,16 @@ struct Bf16Engine {
       }
 #pragma unroll
       for (int j = 0; j < VT; ++j)
-        o[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv.vv[j]),
+        o[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv[j]),
                                                            p, o[nt][j], 0, 0, 0);
     }
+  }
+
+  // A whole loaded step: scores, then softmax and p.V.
+  __device__ __forceinline__ void compute(KV& kv, int t0, int vend, int lane, float sl2e) {
+    f32x4 sa[NT], sb[NT];
+    scores(kv.kA, kv.kB, sa, sb);
+    finish(sa, sb, kv.vv, t0, vend, lane, sl2e);
   }
 
   __device__ __forceinline__ void step(const uint16_t* __restrict__ pool, int64_t blk_elems,
@@ -1125,8 +1143,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
     const int bsl = BS == 16 ? (sl & 3) : sl;
     return vofs + (static_cast<int64_t>(bsl) * D + 2 * dp) * 4;
   };
-  u32x4 pre[kPer];
-  auto fetch = [&](int t0) {  // step at t0 -> registers (t0 < kend_wg)
+  // Steps are fetched two ahead: step s+2's loads go out while step s is
+  // computed, and step s+1, loaded during step s-1, is stored to LDS after it.
+  // Two register sets alternate, so the loop is unrolled by two; every load and
+  // store is issued unconditionally (past the last step they repeat the last
+  // step's addresses into a buffer nobody reads), which keeps the compiler's
+  // wait for step s+1 exact instead of a wait for every load in flight.
+  const int nsteps = (kend_wg + kStep - 1) / kStep;
+  auto fetch = [&](int step, u32x4 (&pre)[kPer]) {  // step -> registers
+    const int t0 = min(step, nsteps - 1) * kStep;
     const int ia = table_entry(trow, t0 / BS);
     const int ib = (BS == 16 && t0 + 16 < kend_wg) ? table_entry(trow, t0 / BS + 1) : ia;
     const uint16_t* bA = pool + clamp_block(ia, a.nb) * a.blk_elems;
@@ -1138,7 +1163,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
       pre[u] = ld16((from_b ? bB : bA) + off);
     }
   };
-  auto stash = [&](int buf) {  // registers -> LDS buffer
+  auto stash = [&](int buf, const u32x4 (&pre)[kPer]) {  // registers -> LDS buffer
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int pc = u * 256 + static_cast<int>(threadIdx.x);
@@ -1146,35 +1171,45 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
       *reinterpret_cast<u32x4*>(dst) = pre[u];
     }
   };
-  auto operands = [&](int buf, typename Eng::KV& kv) {  // LDS -> this lane's MFMA operands
+  // One step from LDS: the K operands feed the scores, then the V operands are
+  // read into registers the K operands no longer need while the softmax runs.
+  auto step = [&](int buf, int t0) {
+    u32x4 kA[KS], kB[KS];
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
-      kv.kA[s2] = *reinterpret_cast<const u32x4*>(&sm.k[buf][((4 * s2 + kg) * kStep + r) * 8]);
-      kv.kB[s2] = *reinterpret_cast<const u32x4*>(&sm.k[buf][((4 * s2 + kg) * kStep + 16 + r) * 8]);
+      kA[s2] = *reinterpret_cast<const u32x4*>(&sm.k[buf][((4 * s2 + kg) * kStep + r) * 8]);
+      kB[s2] = *reinterpret_cast<const u32x4*>(&sm.k[buf][((4 * s2 + kg) * kStep + 16 + r) * 8]);
     }
+    f32x4 sa[NT], sb[NT];
+    eng.scores(kA, kB, sa, sb);
+    u32x4 vv[VT];
 #pragma unroll
     for (int j = 0; j < VT; ++j) {
       const u32x2 lo = *reinterpret_cast<const u32x2*>(&sm.v[buf][(kg * D + 16 * j + r) * 4]);
       const u32x2 hi = *reinterpret_cast<const u32x2*>(&sm.v[buf][((4 + kg) * D + 16 * j + r) * 4]);
-      kv.vv[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      vv[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
+    eng.finish(sa, sb, vv, t0, kend_wg, lane, a.sl2e);
   };
-
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  int buf = 0;
-  for (int t0 = 0; t0 < kend_wg; t0 += kStep) {
-    const bool more = t0 + kStep < kend_wg;
-    if (more) fetch(t0 + kStep);
-    if (i0 < L && t0 < kend) {  // this wave has rows, and they see keys of this step
-      typename Eng::KV kv;
-      operands(buf, kv);
-      eng.compute(kv, t0, kend_wg, lane, a.sl2e);
-    }
-    if (more) stash(buf ^ 1);
+  // Iteration s: fetch step s+2 into `fetch_into` (free: its step s went to
+  // LDS in iteration s-1), compute step s from LDS buffer s&1, store step s+1
+  // from `held` into LDS buffer (s+1)&1 (last read in iteration s-1, before
+  // its barrier), then one barrier.
+  auto iteration = [&](int s, u32x4 (&fetch_into)[kPer], const u32x4 (&held)[kPer]) {
+    fetch(s + 2, fetch_into);
+    const int t0 = s * kStep;
+    if (s < nsteps && i0 < L && t0 < kend) step(s & 1, t0);  // wave-uniform
+    stash((s + 1) & 1, held);
     __syncthreads();
-    buf ^= 1;
+  };
+  u32x4 preA[kPer], preB[kPer];
+  fetch(0, preA);
+  fetch(1, preB);
+  stash(0, preA);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    iteration(s, preA, preB);
+    iteration(s + 1, preB, preA);
   }
   uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
