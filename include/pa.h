@@ -188,6 +188,35 @@ int pa_prefill_chunk(void* out, const void* q, const void* kv_pool,
                      int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                      int32_t dtype, void* stream);
 
+/*
+ * pa_mixed_attention — one iteration's decode batch and prefill chunks
+ * together. (worksonmygpu.com continuous-batching post, "The prefill/decode
+ * mix makes scheduling harder, not easier": prefill chunks and decode steps
+ * share an iteration.)
+ *
+ * Computes exactly what pa_decode (dec_* arguments, workspace) and
+ * pa_prefill_chunk (pre_* arguments) compute on the same pool, with the same
+ * conventions, shapes, errors and results; either side may be empty
+ * (num_seqs == 0, or num_chunks == 0). For bfloat16 batches of at most 2048
+ * sequences and at most 1024 (chunk, position-block) prefill tiles both run
+ * in one persistent launch (plus the decode split-K merge): workgroups take
+ * decode items and prefill tiles from two shared work lists, so the
+ * HBM-bound decode and the MFMA-bound prefill overlap on every CU. Otherwise
+ * the two launches run in turn. Outputs must not overlap each other or either
+ * query buffer (PA_ERR_ALIAS). The workspace is pa_decode's, for the decode
+ * side's shape; its counters also serve the prefill work list.
+ */
+int pa_mixed_attention(void* dec_out, const void* dec_q, const int32_t* dec_block_tables,
+                       const int32_t* dec_context_lens, int32_t num_seqs,
+                       int32_t dec_max_blocks_per_seq, int32_t max_context_len, void* pre_out,
+                       const void* pre_q, const int32_t* pre_block_tables,
+                       const int32_t* pre_context_lens, const int32_t* query_start_loc,
+                       int32_t num_chunks, int32_t total_q_tokens, int32_t max_chunk_len,
+                       int32_t pre_max_blocks_per_seq, const void* kv_pool, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, float scale, int32_t dtype, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* pa_status_string(int status);
 

@@ -17,8 +17,8 @@ import os
 import torch
 
 __all__ = ["PAError", "load", "lib_path", "pa_append_kv", "pa_copy_blocks", "pa_decode",
-           "pa_decode_workspace_size", "pa_prefill_chunk", "pa_status_string",
-           "new_decode_workspace", "DECODE_PARTITION"]
+           "pa_decode_workspace_size", "pa_prefill_chunk", "pa_mixed_attention",
+           "pa_status_string", "new_decode_workspace", "DECODE_PARTITION"]
 
 DECODE_PARTITION = 512  # PA_DECODE_PARTITION in include/pa.h
 
@@ -68,6 +68,12 @@ def load() -> ctypes.CDLL:
                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_int, ctypes.c_float, _c_int, _c_ptr]
     lib.pa_prefill_chunk.restype = ctypes.c_int
+    lib.pa_mixed_attention.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int,
+                                       _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
+                                       _c_int, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
+                                       _c_int, ctypes.c_float, _c_int, _c_ptr, ctypes.c_size_t,
+                                       _c_ptr]
+    lib.pa_mixed_attention.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -188,3 +194,31 @@ def pa_prefill_chunk(out, q, kv_pool, block_tables, context_lens, query_start_lo
         num_kv_heads, d, block_size, nb, float(scale), _dtype_code(q, kv_pool, out),
         _stream(stream)))
     return out
+
+
+def pa_mixed_attention(dec_out, dec_q, dec_tables, dec_lens, max_context_len: int, pre_out,
+                       pre_q, pre_tables, pre_lens, query_start_loc, max_chunk_len: int, kv_pool,
+                       num_kv_heads: int, block_size: int, scale: float, workspace,
+                       stream=None) -> None:
+    """A decode batch and prefill chunks in one call (see include/pa.h); fills both outputs.
+
+    Either side may be empty (a batch of zero sequences, or zero chunks).
+    """
+    B, hq, d = dec_q.shape
+    T = pre_q.shape[0]
+    C = pre_lens.shape[0]
+    nb = _num_blocks(kv_pool, num_kv_heads, block_size, d)
+    dmb = dec_tables.shape[1] if dec_tables.dim() == 2 else 0
+    pmb = pre_tables.shape[1] if pre_tables.dim() == 2 else 0
+    dec_ok, pre_ok = B > 0, C > 0 and T > 0
+    _check("pa_mixed_attention", load().pa_mixed_attention(
+        _dev(dec_out, "dec_out") if dec_ok else None, _dev(dec_q, "dec_q") if dec_ok else None,
+        _i32(dec_tables, "dec_tables") if dec_ok else None,
+        _i32(dec_lens, "dec_lens") if dec_ok else None, B, dmb, int(max_context_len),
+        _dev(pre_out, "pre_out") if pre_ok else None, _dev(pre_q, "pre_q") if pre_ok else None,
+        _i32(pre_tables, "pre_tables") if pre_ok else None,
+        _i32(pre_lens, "pre_lens") if pre_ok else None,
+        _i32(query_start_loc, "query_start_loc") if pre_ok else None, C, T, int(max_chunk_len),
+        pmb, _dev(kv_pool, "kv_pool"), hq, num_kv_heads, d, block_size, nb, float(scale),
+        _dtype_code(dec_q, kv_pool), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -95,15 +95,17 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
       .total;
 }
 
-int pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
-              const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-              int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
-              int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-              int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (num_seqs < 0 || max_blocks_per_seq < 0 || max_context_len < 0) return PA_ERR_SHAPE;
-  if (int s = check_pool(num_blocks, num_kv_heads, head_dim, block_size, dtype)) return s;
-  if (int s = check_heads(num_q_heads, num_kv_heads)) return s;
-  if (num_seqs == 0) return PA_OK;
+}  // extern "C"
+
+namespace {
+
+// Host checks of a decode batch with at least one sequence (pool and heads
+// already checked).
+int check_decode(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                 const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                 int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t block_size, int32_t dtype, void* workspace,
+                 size_t workspace_bytes) {
   if (!out || !q || !kv_pool || !block_tables || !context_lens || !workspace) return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(kv_pool) || !aligned16(workspace))
     return PA_ERR_ALIGN;
@@ -116,6 +118,43 @@ int pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* bloc
     return PA_ERR_WORKSPACE;
   const size_t qbytes = size_t(num_seqs) * num_q_heads * head_dim * elem_bytes(dtype);
   if (overlaps(out, qbytes, q, qbytes)) return PA_ERR_ALIAS;
+  return PA_OK;
+}
+
+// Host checks of a prefill batch with at least one chunk and token.
+int check_prefill(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                  const int32_t* context_lens, const int32_t* query_start_loc,
+                  int32_t num_chunks, int32_t total_q_tokens, int32_t max_chunk_len,
+                  int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t dtype) {
+  if (!out || !q || !kv_pool || !block_tables || !context_lens || !query_start_loc)
+    return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(kv_pool)) return PA_ERR_ALIGN;
+  if (max_blocks_per_seq <= 0 || max_chunk_len <= 0 || max_chunk_len > total_q_tokens)
+    return PA_ERR_SHAPE;
+  if (num_chunks > 65535 || num_kv_heads > 65535) return PA_ERR_SHAPE;  // grid y/z limits
+  const size_t qbytes = size_t(total_q_tokens) * num_q_heads * head_dim * elem_bytes(dtype);
+  if (overlaps(out, qbytes, q, qbytes)) return PA_ERR_ALIAS;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+              const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+              int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+              int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+              int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || max_context_len < 0) return PA_ERR_SHAPE;
+  if (int s = check_pool(num_blocks, num_kv_heads, head_dim, block_size, dtype)) return s;
+  if (int s = check_heads(num_q_heads, num_kv_heads)) return s;
+  if (num_seqs == 0) return PA_OK;
+  if (int s = check_decode(out, q, kv_pool, block_tables, context_lens, num_seqs,
+                           max_blocks_per_seq, max_context_len, num_q_heads, num_kv_heads,
+                           head_dim, block_size, dtype, workspace, workspace_bytes))
+    return s;
   return status_of(pa::launch_decode(out, q, kv_pool, block_tables, context_lens, num_seqs,
                                      max_blocks_per_seq, max_context_len, num_q_heads,
                                      shape(num_blocks, num_kv_heads, head_dim, block_size), scale,
@@ -134,19 +173,63 @@ int pa_prefill_chunk(void* out, const void* q, const void* kv_pool,
   if (int s = check_pool(num_blocks, num_kv_heads, head_dim, block_size, dtype)) return s;
   if (int s = check_heads(num_q_heads, num_kv_heads)) return s;
   if (num_chunks == 0 || total_q_tokens == 0) return PA_OK;
-  if (!out || !q || !kv_pool || !block_tables || !context_lens || !query_start_loc)
-    return PA_ERR_NULL;
-  if (!aligned16(out) || !aligned16(q) || !aligned16(kv_pool)) return PA_ERR_ALIGN;
-  if (max_blocks_per_seq <= 0 || max_chunk_len <= 0 || max_chunk_len > total_q_tokens)
-    return PA_ERR_SHAPE;
-  if (num_chunks > 65535 || num_kv_heads > 65535) return PA_ERR_SHAPE;  // grid y/z limits
-  const size_t qbytes = size_t(total_q_tokens) * num_q_heads * head_dim * elem_bytes(dtype);
-  if (overlaps(out, qbytes, q, qbytes)) return PA_ERR_ALIAS;
+  if (int s = check_prefill(out, q, kv_pool, block_tables, context_lens, query_start_loc,
+                            num_chunks, total_q_tokens, max_chunk_len, max_blocks_per_seq,
+                            num_q_heads, num_kv_heads, head_dim, dtype))
+    return s;
   return status_of(pa::launch_prefill(out, q, kv_pool, block_tables, context_lens,
                                       query_start_loc, num_chunks, total_q_tokens, max_chunk_len,
                                       max_blocks_per_seq, num_q_heads,
                                       shape(num_blocks, num_kv_heads, head_dim, block_size),
                                       scale, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int pa_mixed_attention(void* dec_out, const void* dec_q, const int32_t* dec_block_tables,
+                       const int32_t* dec_context_lens, int32_t num_seqs,
+                       int32_t dec_max_blocks_per_seq, int32_t max_context_len, void* pre_out,
+                       const void* pre_q, const int32_t* pre_block_tables,
+                       const int32_t* pre_context_lens, const int32_t* query_start_loc,
+                       int32_t num_chunks, int32_t total_q_tokens, int32_t max_chunk_len,
+                       int32_t pre_max_blocks_per_seq, const void* kv_pool, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, float scale, int32_t dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || dec_max_blocks_per_seq < 0 || max_context_len < 0 || num_chunks < 0 ||
+      total_q_tokens < 0 || max_chunk_len < 0 || pre_max_blocks_per_seq < 0)
+    return PA_ERR_SHAPE;
+  if (int s = check_pool(num_blocks, num_kv_heads, head_dim, block_size, dtype)) return s;
+  if (int s = check_heads(num_q_heads, num_kv_heads)) return s;
+  const bool dec = num_seqs > 0, pre = num_chunks > 0 && total_q_tokens > 0;
+  if (dec) {
+    if (int s = check_decode(dec_out, dec_q, kv_pool, dec_block_tables, dec_context_lens,
+                             num_seqs, dec_max_blocks_per_seq, max_context_len, num_q_heads,
+                             num_kv_heads, head_dim, block_size, dtype, workspace,
+                             workspace_bytes))
+      return s;
+  }
+  if (pre) {
+    if (int s = check_prefill(pre_out, pre_q, kv_pool, pre_block_tables, pre_context_lens,
+                              query_start_loc, num_chunks, total_q_tokens, max_chunk_len,
+                              pre_max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim,
+                              dtype))
+      return s;
+  }
+  if (dec && pre) {  // neither output may overlap the other call's output or query
+    const size_t e = elem_bytes(dtype);
+    const size_t db = size_t(num_seqs) * num_q_heads * head_dim * e;
+    const size_t pb = size_t(total_q_tokens) * num_q_heads * head_dim * e;
+    if (overlaps(dec_out, db, pre_out, pb) || overlaps(dec_out, db, pre_q, pb) ||
+        overlaps(pre_out, pb, dec_q, db))
+      return PA_ERR_ALIAS;
+  }
+  if (!dec && !pre) return PA_OK;
+  return status_of(pa::launch_mixed(
+      dec_out, dec_q, kv_pool, dec_block_tables, dec_context_lens, num_seqs,
+      dec_max_blocks_per_seq, max_context_len, pre_out, pre_q, pre_block_tables,
+      pre_context_lens, query_start_loc, pre ? num_chunks : 0, total_q_tokens,
+      pre ? max_chunk_len : 0, pre_max_blocks_per_seq, num_q_heads,
+      shape(num_blocks, num_kv_heads, head_dim, block_size), scale, dtype, workspace,
+      static_cast<hipStream_t>(stream)));
 }
 
 const char* pa_status_string(int status) {

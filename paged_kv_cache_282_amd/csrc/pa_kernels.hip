@@ -736,16 +736,39 @@ __device__ __forceinline__ void make_uniform(QItem& it) {
 // queue) reads block 0, which stays cached, and is never computed. Loads
 // inside branches would make the compiler's wait counts conservative (wait for
 // all outstanding loads), which serialises loads and compute.
+template <int D>
+struct DecodeSmem {
+  MergeSmem<D> sm2[2];  // wave states of consecutive items alternate
+  ScanSmem sc;
+  int s_next[2];
+};
+
+// The queue counters live at the start of the decode workspace: [0] the next
+// decode item, [1] workgroups that have left, [2] the next prefill tile of a
+// mixed launch. The last workgroup to leave returns them to zero.
+__device__ __forceinline__ void leave_queue(int32_t* __restrict__ queue) {
+  if (threadIdx.x == 0) {
+    const int done = atomicAdd(&queue[1], 1);
+    if (done == static_cast<int>(gridDim.x) - 1) {  // everyone else has left
+      atomicExch(&queue[0], 0);
+      atomicExch(&queue[2], 0);
+      atomicExch(&queue[1], 0);
+    }
+  }
+}
+
+// The whole decode pipeline of one workgroup: takes items until the queue
+// runs past the last one. Every workgroup of the grid runs it.
 template <int D, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
+__device__ __forceinline__ void decode_persistent(const DecodeArgs& a, int32_t* __restrict__ queue,
+                                                  DecodeSmem<D>& ds) {
   using Eng = Bf16Engine<D, BS, 1>;
   constexpr int KS = Eng::KS;
   constexpr int kSteps = kPartition / (kWaves * kStep);  // steps per wave per partition
   static_assert(kSteps % 2 == 0, "steps alternate between two register buffers");
-  __shared__ MergeSmem<D> sm2[2];  // wave states of consecutive items alternate
-  __shared__ ScanSmem sc;
-  __shared__ int s_next[2];
+  MergeSmem<D>(&sm2)[2] = ds.sm2;
+  ScanSmem& sc = ds.sc;
+  int(&s_next)[2] = ds.s_next;
   const int B = a.num_seqs;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -931,13 +954,14 @@ void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
     nxt_k = after_k;
   }
   if (have_prev) publish(sm2[parity ^ 1], prev);
-  if (threadIdx.x == 0) {
-    const int done = atomicAdd(&queue[1], 1);
-    if (done == static_cast<int>(gridDim.x) - 1) {  // everyone else has left
-      atomicExch(&queue[0], 0);
-      atomicExch(&queue[1], 0);
-    }
-  }
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
+  __shared__ DecodeSmem<D> ds;
+  decode_persistent<D, BS>(a, queue, ds);
+  leave_queue(queue);
 }
 
 template <int D, int BS, int G>
@@ -1088,7 +1112,7 @@ struct PrefillSmem {
 // Every branch that returns early is uniform over the workgroup, and every
 // path that reaches the step loop runs the same barriers in every wave.
 template <int D, int BS, int NT>
-__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D>& sm, int x,
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D>& smem, int x,
                                              int c, int g) {
   using Eng = Bf16Engine<D, BS, NT>;
   constexpr int KS = Eng::KS, VT = Eng::VT;
@@ -1107,6 +1131,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
   const int r = lane & 15, kg = lane >> 4;
   const uint16_t* pool = static_cast<const uint16_t*>(a.pool);
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  // the two LDS buffers, through pointers that alias nothing else
+  constexpr int kK = (D / 8) * kStep * 8, kV = (kStep / 4) * D * 4;
+  uint16_t* __restrict__ lk = &smem.k[0][0];
+  uint16_t* __restrict__ lv = &smem.v[0][0];
 
   Eng eng;
   eng.init();
@@ -1167,7 +1195,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int pc = u * 256 + static_cast<int>(threadIdx.x);
-      uint16_t* dst = pc < kChunks / 2 ? &sm.k[buf][pc * 8] : &sm.v[buf][(pc - kChunks / 2) * 8];
+      uint16_t* dst = pc < kChunks / 2 ? &lk[buf * kK + pc * 8] : &lv[buf * kV + (pc - kChunks / 2) * 8];
       *reinterpret_cast<u32x4*>(dst) = pre[u];
     }
   };
@@ -1177,16 +1205,16 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
     u32x4 kA[KS], kB[KS];
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
-      kA[s2] = *reinterpret_cast<const u32x4*>(&sm.k[buf][((4 * s2 + kg) * kStep + r) * 8]);
-      kB[s2] = *reinterpret_cast<const u32x4*>(&sm.k[buf][((4 * s2 + kg) * kStep + 16 + r) * 8]);
+      kA[s2] = *reinterpret_cast<const u32x4*>(&lk[buf * kK + ((4 * s2 + kg) * kStep + r) * 8]);
+      kB[s2] = *reinterpret_cast<const u32x4*>(&lk[buf * kK + ((4 * s2 + kg) * kStep + 16 + r) * 8]);
     }
     f32x4 sa[NT], sb[NT];
     eng.scores(kA, kB, sa, sb);
     u32x4 vv[VT];
 #pragma unroll
     for (int j = 0; j < VT; ++j) {
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(&sm.v[buf][(kg * D + 16 * j + r) * 4]);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(&sm.v[buf][((4 + kg) * D + 16 * j + r) * 4]);
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(&lv[buf * kV + (kg * D + 16 * j + r) * 4]);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(&lv[buf * kV + ((4 + kg) * D + 16 * j + r) * 4]);
       vv[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
     eng.finish(sa, sb, vv, t0, kend_wg, lane, a.sl2e);
@@ -1248,12 +1276,19 @@ void prefill_bf16_kernel(PrefillArgs a) {
 // which keeps the longest tiles from ending up on the same workgroups.
 constexpr int kMaxPrefillTiles = 1024;  // (chunk, x) pairs ranked in LDS
 
-template <int D, int BS, int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_bf16_lpt_kernel(PrefillArgs a, int gx) {
-  __shared__ PrefillSmem<D> sm;
-  __shared__ int s_key[kMaxPrefillTiles];
-  __shared__ int s_order[kMaxPrefillTiles];
+template <int D>
+struct PrefillLds {
+  PrefillSmem<D> sm;
+  int key[kMaxPrefillTiles];    // key steps of (chunk, x) pair i = c * gx + x
+  int order[kMaxPrefillTiles];  // pairs by decreasing key
+  int next;
+};
+
+// Ranks the (chunk, x) pairs by their number of key steps; returns how many
+// pairs there are. Ends with a barrier.
+template <int BS, int NT>
+__device__ __forceinline__ int prefill_rank(const PrefillArgs& a, int gx, int* __restrict__ key_of,
+                                            int* __restrict__ order) {
   const int M = a.num_chunks * gx;
   const int G = a.hq / a.hkv;
   const int pos_per_wg = kWaves * 16 * NT / G;
@@ -1262,20 +1297,29 @@ void prefill_bf16_lpt_kernel(PrefillArgs a, int gx) {
     int q0, L, prior, key = 0;
     if (chunk_geometry(a, c, a.mb * BS, q0, L, prior) && x * pos_per_wg < L)
       key = (prior + min(L, (x + 1) * pos_per_wg) + kStep - 1) / kStep;
-    s_key[i] = key;
+    key_of[i] = key;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < M; i += kWaves * 64) {
-    const int ki = s_key[i];
+    const int ki = key_of[i];
     int rank = 0;
     for (int j = 0; j < M; ++j) {
-      const int kj = s_key[j];
+      const int kj = key_of[j];
       rank += (kj > ki || (kj == ki && j < i)) ? 1 : 0;
     }
-    s_order[rank] = i;
+    order[rank] = i;
   }
   __syncthreads();
-  const int tiles = M * a.hkv;
+  return M;
+}
+
+template <int D, int BS, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_bf16_lpt_kernel(PrefillArgs a, int gx) {
+  __shared__ PrefillSmem<D> sm;
+  __shared__ int s_key[kMaxPrefillTiles];
+  __shared__ int s_order[kMaxPrefillTiles];
+  const int tiles = prefill_rank<BS, NT>(a, gx, s_key, s_order) * a.hkv;
   const int P = static_cast<int>(gridDim.x);
   for (int k = 0; k * P < tiles; ++k) {
     const int t = k * P + ((k & 1) ? P - 1 - static_cast<int>(blockIdx.x)
@@ -1285,6 +1329,59 @@ void prefill_bf16_lpt_kernel(PrefillArgs a, int gx) {
     if (s_key[combo] == 0) break;  // sorted: every later tile is empty too
     prefill_tile<D, BS, NT>(a, sm, combo % gx, combo / gx, t % a.hkv);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Mixed batch: decode sequences and prefill chunks in one persistent launch.
+//
+// The workgroups share two work lists: decode items from the decode queue and
+// prefill tiles, longest first, from a second counter. The grid holds two
+// workgroups per CU; the first half of the grid (one per CU, as the
+// dispatcher fills every CU's first slot before any second one) starts on
+// prefill tiles and the second half on decode items, and each turns to the
+// other list when its first one runs dry. So while both lists last, a CU
+// holds one workgroup of each kind: the HBM-bound decode steps and the
+// MFMA-bound prefill steps overlap instead of running back to back. The
+// split-K merge of long decode sequences still follows as its own kernel.
+// ---------------------------------------------------------------------------
+template <int D>
+union MixedSmem {
+  DecodeSmem<D> d;
+  PrefillLds<D> p;
+};
+
+template <int D, int BS, int NT>
+__device__ __forceinline__ void prefill_from_queue(const PrefillArgs& a, int gx,
+                                                   int32_t* __restrict__ queue,
+                                                   PrefillLds<D>& ps) {
+  const int tiles = prefill_rank<BS, NT>(a, gx, ps.key, ps.order) * a.hkv;
+  for (;;) {
+    if (threadIdx.x == 0) ps.next = atomicAdd(&queue[2], 1);
+    __syncthreads();
+    const int t = ps.next;
+    __syncthreads();  // read before the next tile's thread 0 rewrites it
+    if (t >= tiles) break;
+    const int combo = ps.order[t / a.hkv];
+    if (ps.key[combo] == 0) break;  // sorted: every later tile is empty too
+    prefill_tile<D, BS, NT>(a, ps.sm, combo % gx, combo / gx, t % a.hkv);
+  }
+}
+
+template <int D, int BS, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mixed_bf16_kernel(DecodeArgs da, PrefillArgs pa, int gx, int32_t* __restrict__ queue) {
+  __shared__ MixedSmem<D> u;
+  const bool prefill_first = blockIdx.x < gridDim.x / 2;
+  if (prefill_first) {
+    if (pa.num_chunks > 0) prefill_from_queue<D, BS, NT>(pa, gx, queue, u.p);
+    __syncthreads();  // LDS changes hands
+    if (da.num_seqs > 0) decode_persistent<D, BS>(da, queue, u.d);
+  } else {
+    if (da.num_seqs > 0) decode_persistent<D, BS>(da, queue, u.d);
+    __syncthreads();
+    if (pa.num_chunks > 0) prefill_from_queue<D, BS, NT>(pa, gx, queue, u.p);
+  }
+  leave_queue(queue);
 }
 
 // fp32: one workgroup per (position, chunk, kv head); its waves split the keys.
@@ -1547,11 +1644,12 @@ hipError_t launch_copy(void* pool, const int32_t* pairs, int num_pairs, const Po
   return hipGetLastError();
 }
 
-hipError_t launch_decode(void* out, const void* q, const void* pool, const int32_t* tables,
-                         const int32_t* lens, int num_seqs, int max_blocks_per_seq,
-                         int max_context_len, int num_q_heads, const PoolShape& ps, float scale,
-                         int dtype, void* workspace, hipStream_t st) {
-  if (num_seqs == 0) return hipSuccess;
+namespace {
+
+DecodeArgs decode_args(void* out, const void* q, const void* pool, const int32_t* tables,
+                       const int32_t* lens, int num_seqs, int max_blocks_per_seq,
+                       int max_context_len, int num_q_heads, const PoolShape& ps, float scale,
+                       void* workspace, int32_t*& queue) {
   const int64_t np_max = decode_max_parts(max_context_len);
   const DecodeWorkspace wl = DecodeWorkspace::layout(num_seqs, num_q_heads, ps.head_dim, np_max);
   DecodeArgs a;
@@ -1571,10 +1669,56 @@ hipError_t launch_decode(void* out, const void* q, const void* pool, const int32
   a.sl2e = scale * kLog2e;
   a.ws_o = static_cast<char*>(workspace) + wl.o_off;
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
-  int32_t* queue = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.queue_off);
-  const int64_t items = static_cast<int64_t>(num_seqs) * ps.num_kv_heads * np_max;
-  a.n_items = static_cast<int>(items);
-  const int grid = static_cast<int>(items);
+  queue = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.queue_off);
+  a.n_items = static_cast<int>(static_cast<int64_t>(num_seqs) * ps.num_kv_heads * np_max);
+  return a;
+}
+
+PrefillArgs prefill_args(void* out, const void* q, const void* pool, const int32_t* tables,
+                         const int32_t* lens, const int32_t* qsl, int num_chunks,
+                         int total_q_tokens, int max_blocks_per_seq, int num_q_heads,
+                         const PoolShape& ps, float scale) {
+  PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.pool = pool;
+  a.tables = tables;
+  a.lens = lens;
+  a.qsl = qsl;
+  a.num_chunks = num_chunks;
+  a.total_q = total_q_tokens;
+  a.mb = max_blocks_per_seq;
+  a.hq = num_q_heads;
+  a.hkv = ps.num_kv_heads;
+  a.nb = ps.num_blocks;
+  a.blk_elems = ps.block_elems();
+  a.sl2e = scale * kLog2e;
+  return a;
+}
+
+template <int D, int BS>
+hipError_t launch_mixed_bf16(const DecodeArgs& da, const PrefillArgs& pa, int gx, int32_t* queue,
+                             hipStream_t st) {
+  static const int resident = resident_workgroups(mixed_bf16_kernel<D, BS, kPrefillNT>);
+  hipLaunchKernelGGL((mixed_bf16_kernel<D, BS, kPrefillNT>), dim3(resident > 0 ? resident : 512),
+                     dim3(256), 0, st, da, pa, gx, queue);
+  if (da.num_seqs > 0 && da.np_max > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<D, BS, uint16_t>), dim3(da.num_seqs * da.hkv),
+                       dim3(256), 0, st, da);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(void* out, const void* q, const void* pool, const int32_t* tables,
+                         const int32_t* lens, int num_seqs, int max_blocks_per_seq,
+                         int max_context_len, int num_q_heads, const PoolShape& ps, float scale,
+                         int dtype, void* workspace, hipStream_t st) {
+  if (num_seqs == 0) return hipSuccess;
+  int32_t* queue = nullptr;
+  const DecodeArgs a = decode_args(out, q, pool, tables, lens, num_seqs, max_blocks_per_seq,
+                                   max_context_len, num_q_heads, ps, scale, workspace, queue);
+  const int grid = a.n_items;
   const int G = num_q_heads / ps.num_kv_heads;
   const int D = ps.head_dim, BS = ps.block_size;
   if (dtype == 1) {
@@ -1597,21 +1741,8 @@ hipError_t launch_prefill(void* out, const void* q, const void* pool, const int3
                           int num_q_heads,
                           const PoolShape& ps, float scale, int dtype, hipStream_t st) {
   if (num_chunks == 0 || max_chunk_len == 0) return hipSuccess;
-  PrefillArgs a;
-  a.out = out;
-  a.q = q;
-  a.pool = pool;
-  a.tables = tables;
-  a.lens = lens;
-  a.qsl = qsl;
-  a.num_chunks = num_chunks;
-  a.total_q = total_q_tokens;
-  a.mb = max_blocks_per_seq;
-  a.hq = num_q_heads;
-  a.hkv = ps.num_kv_heads;
-  a.nb = ps.num_blocks;
-  a.blk_elems = ps.block_elems();
-  a.sl2e = scale * kLog2e;
+  const PrefillArgs a = prefill_args(out, q, pool, tables, lens, qsl, num_chunks, total_q_tokens,
+                                     max_blocks_per_seq, num_q_heads, ps, scale);
   const int D = ps.head_dim, BS = ps.block_size;
   if (dtype == 1) {
     if (D == 64 && BS == 16) return launch_prefill_bf16<64, 16>(a, max_chunk_len, st);
@@ -1624,6 +1755,42 @@ hipError_t launch_prefill(void* out, const void* q, const void* pool, const int3
     if (D == 128 && BS == 16) return launch_prefill_f32<128, 16>(a, max_chunk_len, st);
     if (D == 128 && BS == 32) return launch_prefill_f32<128, 32>(a, max_chunk_len, st);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mixed(void* dec_out, const void* dec_q, const void* pool,
+                        const int32_t* dec_tables, const int32_t* dec_lens, int num_seqs,
+                        int dec_max_blocks, int max_context_len, void* pre_out,
+                        const void* pre_q, const int32_t* pre_tables, const int32_t* pre_lens,
+                        const int32_t* qsl, int num_chunks, int total_q_tokens, int max_chunk_len,
+                        int pre_max_blocks, int num_q_heads, const PoolShape& ps, float scale,
+                        int dtype, void* workspace, hipStream_t st) {
+  const int G = num_q_heads / ps.num_kv_heads;
+  const int pos_per_wg = kWaves * 16 * kPrefillNT / G;
+  const int64_t gx = num_chunks > 0 ? (max_chunk_len + pos_per_wg - 1) / pos_per_wg : 0;
+  const bool fused = dtype == 1 && num_seqs <= kMaxScanSeqs && gx * num_chunks <= kMaxPrefillTiles;
+  if (!fused || num_seqs == 0 || num_chunks == 0 || max_chunk_len == 0) {
+    // one kind of work only, or shapes the fused kernel does not take: the
+    // two launches in turn
+    if (hipError_t e = launch_decode(dec_out, dec_q, pool, dec_tables, dec_lens, num_seqs,
+                                     dec_max_blocks, max_context_len, num_q_heads, ps, scale,
+                                     dtype, workspace, st))
+      return e;
+    return launch_prefill(pre_out, pre_q, pool, pre_tables, pre_lens, qsl, num_chunks,
+                          total_q_tokens, max_chunk_len, pre_max_blocks, num_q_heads, ps, scale,
+                          dtype, st);
+  }
+  int32_t* queue = nullptr;
+  const DecodeArgs da =
+      decode_args(dec_out, dec_q, pool, dec_tables, dec_lens, num_seqs, dec_max_blocks,
+                  max_context_len, num_q_heads, ps, scale, workspace, queue);
+  const PrefillArgs pa = prefill_args(pre_out, pre_q, pool, pre_tables, pre_lens, qsl, num_chunks,
+                                      total_q_tokens, pre_max_blocks, num_q_heads, ps, scale);
+  const int D = ps.head_dim, BS = ps.block_size, gxi = static_cast<int>(gx);
+  if (D == 64 && BS == 16) return launch_mixed_bf16<64, 16>(da, pa, gxi, queue, st);
+  if (D == 64 && BS == 32) return launch_mixed_bf16<64, 32>(da, pa, gxi, queue, st);
+  if (D == 128 && BS == 16) return launch_mixed_bf16<128, 16>(da, pa, gxi, queue, st);
+  if (D == 128 && BS == 32) return launch_mixed_bf16<128, 32>(da, pa, gxi, queue, st);
   return hipErrorInvalidValue;
 }
 

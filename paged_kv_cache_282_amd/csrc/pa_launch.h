@@ -64,4 +64,14 @@ hipError_t launch_prefill(void* out, const void* q, const void* pool, const int3
                           int total_q_tokens, int max_chunk_len, int max_blocks_per_seq, int num_q_heads,
                           const PoolShape& ps, float scale, int dtype, hipStream_t stream);
 
+// Decode batch and prefill chunks in one persistent launch (bf16, batches the
+// fused kernel takes), else the two launches in turn.
+hipError_t launch_mixed(void* dec_out, const void* dec_q, const void* pool,
+                        const int32_t* dec_tables, const int32_t* dec_lens, int num_seqs,
+                        int dec_max_blocks, int max_context_len, void* pre_out,
+                        const void* pre_q, const int32_t* pre_tables, const int32_t* pre_lens,
+                        const int32_t* qsl, int num_chunks, int total_q_tokens, int max_chunk_len,
+                        int pre_max_blocks, int num_q_heads, const PoolShape& ps, float scale,
+                        int dtype, void* workspace, hipStream_t stream);
+
 }  // namespace pa

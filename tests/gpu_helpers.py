@@ -76,6 +76,13 @@ class DeviceStep:
                                    self.qsl, self.max_chunk, w.num_kv_heads, w.block_size,
                                    w.scale)
 
+    def mixed(self, out, pout):
+        """Decode and prefill of this step in one pa_mixed_attention call."""
+        w = self.w
+        pa.pa_mixed_attention(out, self.q, self.tables, self.lens, w.max_context_len, pout,
+                              self.pq, self.ptables, self.plens, self.qsl, self.max_chunk,
+                              self.pool, w.num_kv_heads, w.block_size, w.scale, self.ws)
+
     def run(self):
         self.copy()
         self.append()

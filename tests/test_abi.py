@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["pa_append_kv", "pa_copy_blocks", "pa_decode",
                             "pa_decode_workspace_size", "pa_prefill_chunk",
-                            "pa_status_string"])
+                            "pa_mixed_attention", "pa_status_string"])
 
 
 def test_runtime_header_declares_the_runtime():
@@ -160,3 +160,27 @@ def test_engine_validation(lib):
     assert lib.pa_engine_step(None, None, 0, None) == NULL
     assert lib.pa_engine_run(None, None) == NULL
     s.close()
+
+
+def test_mixed_validation(lib):
+    def call(**kw):
+        a = dict(dout=FAKE, dq=FAKE2, dt=FAKE, dl=FAKE, B=2, dmb=4, maxctx=64,
+                 pout=ctypes.c_void_p(0x200000), pq=ctypes.c_void_p(0x300000), pt=FAKE,
+                 pl=FAKE, qsl=FAKE, C=2, T=40, maxL=30, pmb=8, pool=FAKE, hq=8, hkv=2, d=128,
+                 bs=16, nb=20, scale=0.1, dtype=BF16, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return lib.pa_mixed_attention(a["dout"], a["dq"], a["dt"], a["dl"], a["B"], a["dmb"],
+                                      a["maxctx"], a["pout"], a["pq"], a["pt"], a["pl"],
+                                      a["qsl"], a["C"], a["T"], a["maxL"], a["pmb"], a["pool"],
+                                      a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["scale"],
+                                      a["dtype"], a["ws"], a["wsb"], None)
+    assert call(B=0, C=0) == OK                       # nothing to do
+    assert call(B=-1) == SHAPE
+    assert call(d=96) == UNSUPPORTED
+    assert call(dout=None) == NULL
+    assert call(qsl=None) == NULL
+    assert call(wsb=16) == WORKSPACE
+    assert call(maxL=41) == SHAPE
+    assert call(pout=FAKE) == ALIAS                   # prefill output over the decode output
+    assert call(pout=FAKE2) == ALIAS                  # prefill output over the decode query
+    assert call(dq=ctypes.c_void_p(0x200000)) == ALIAS  # decode query over the prefill output

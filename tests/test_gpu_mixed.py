@@ -1,0 +1,103 @@
+"""pa_mixed_attention: a decode batch and prefill chunks in one call.
+
+Per item, the fused launch runs the same decode and prefill code as
+pa_decode and pa_prefill_chunk, so its outputs must equal theirs bit for bit;
+they are also checked against the oracle. Cases cover the fused bf16 path at
+small and full size (the mixed continuous-batching iteration: 240 decode
+sequences and 16 chunks of 512 queries), the fp32 path (two launches in
+turn), one-sided calls, and repeated calls that reuse the workspace counters.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_helpers import (TOL, DeviceStep, bits, max_err, oracle_decode, oracle_pool_after,
+                               oracle_prefill, values)
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+SMALL = dict(num_decode=10, dec_min=1, dec_max=1200, num_chunks=4, chunk_len=100,
+             max_prior=700, num_q_heads=8, num_kv_heads=2)
+
+
+def _run_both(w, label, oracle_check=True, repeats=2):
+    print(f"[case] {label}: decode B={w.num_seqs}, {len(w.prefill_context_lens)} chunks, "
+          f"{w.dtype}", flush=True)
+    st = DeviceStep(w)
+    st.copy()
+    st.append()
+    st.decode()
+    st.prefill()
+    torch.cuda.synchronize()
+    sep_dec, sep_pre = bits(st.out).copy(), bits(st.pout).copy()
+    for _ in range(repeats):   # the workspace counters must be back at zero after each call
+        out = torch.full_like(st.out, float("nan"))
+        pout = torch.full_like(st.pout, float("nan"))
+        st.mixed(out, pout)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), sep_dec), "decode differs from pa_decode"
+        assert np.array_equal(bits(pout), sep_pre), "prefill differs from pa_prefill_chunk"
+    if oracle_check:
+        pool = oracle_pool_after(w)
+        err = max_err(values(out), oracle_decode(w, pool))
+        perr = max_err(values(pout), oracle_prefill(w, pool))
+        print(f"  decode err {err:.3e}, prefill err {perr:.3e}", flush=True)
+        assert err <= TOL[w.dtype] and perr <= TOL[w.dtype]
+    return st
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d,bs", [(128, 16), (64, 32)])
+def test_mixed_matches_separate_calls(dtype, d, bs):
+    w = make_workload("mixed", dtype=dtype, seed=300 + d + bs, head_dim=d, block_size=bs,
+                      **SMALL)
+    _run_both(w, f"mixed-{dtype}-d{d}-bs{bs}")
+
+
+def test_mixed_full_size_iteration():
+    w = make_workload("mixed")
+    _run_both(w, "mixed-full", oracle_check=False)
+    # the oracle on a sample: the first 8 decode sequences and chunk 0
+    st = DeviceStep(w)
+    st.copy()
+    st.append()
+    out, pout = torch.empty_like(st.out), torch.empty_like(st.pout)
+    st.mixed(out, pout)
+    torch.cuda.synchronize()
+    pool = oracle_pool_after(w)
+    idx = np.arange(8)
+    assert max_err(values(out)[idx], oracle_decode(w, pool, idx)) <= TOL["bf16"]
+    import oracle
+    L0 = int(w.query_start_loc[1])
+    want = oracle.prefill(w.prefill_q[:L0], pool, w.prefill_block_tables[:1],
+                          w.prefill_context_lens[:1], w.query_start_loc[:2], w.num_kv_heads,
+                          w.block_size, w.scale, w.dtype)
+    assert max_err(values(pout)[:L0], want) <= TOL["bf16"]
+
+
+def test_mixed_one_sided_calls():
+    import paged_kv_cache_282_amd as pa
+    w = make_workload("mixed", seed=77, **SMALL)
+    st = DeviceStep(w)
+    st.copy()
+    st.append()
+    st.decode()
+    st.prefill()
+    torch.cuda.synchronize()
+    sep_dec, sep_pre = bits(st.out).copy(), bits(st.pout).copy()
+    empty_q = st.q[:0]
+    out = torch.empty_like(st.out)
+    # decode only: zero chunks
+    pa.pa_mixed_attention(out, st.q, st.tables, st.lens, w.max_context_len, st.pout[:0],
+                          st.pq[:0], st.ptables[:0], st.plens[:0], st.qsl[:1], 0, st.pool,
+                          w.num_kv_heads, w.block_size, w.scale, st.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), sep_dec)
+    # prefill only: zero decode sequences
+    pout = torch.empty_like(st.pout)
+    pa.pa_mixed_attention(out[:0], empty_q, st.tables[:0], st.lens[:0], w.max_context_len, pout,
+                          st.pq, st.ptables, st.plens, st.qsl, st.max_chunk, st.pool,
+                          w.num_kv_heads, w.block_size, w.scale, st.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(pout), sep_pre)
