@@ -22,7 +22,8 @@ Reported (one JSON line on stdout):
   rows       every step of the hot path on its own workload: append, block copy,
              decode on the other batches, chunked prefill -- time, algorithmic
              bytes or flops, fraction of the matching roofline, and the oracle's
-             rate on a bounded sample of the same inputs
+             rate on a bounded sample of the same inputs; and the mixed
+             iteration's decode and prefill in one pa_mixed_attention call
   cpu_baseline  the fp64 NumPy oracle on one full headline layer, 1 thread
   engine     the C++ block manager + iteration-level scheduler driving these
              kernels on a long-tail request stream, under paged allocation,
@@ -353,7 +354,30 @@ class Rows:
                      self._oracle(orc, flops0 / 1e12, "TFLOP/s",
                                   "chunk 0 only (512 queries), fp64 NumPy, 1 BLAS thread"),
                      flops_note="4*d per (query, head, attended key): q.k and p.v")
-        del d, w, pq, pout
+
+        # -- the same decode batch and prefill chunks in one pa_mixed_attention call --------
+        out2, pout2 = self.torch.empty_like(d["out"]), self.torch.empty_like(pout)
+
+        def mixed():
+            pa.pa_mixed_attention(out2, d["q"], d["tables"], d["lens"], w.max_context_len, pout2,
+                                  pq, pt, pl, qsl, max_chunk, d["pool"], w.num_kv_heads,
+                                  w.block_size, w.scale, d["ws"])
+
+        ms = time_calls(mixed, self.torch, self.repeats)
+        sep = self.out["a3_a7_decode_mixed"]["us"] + self.out["a8_prefill_chunk"]["us"]
+        bound_us = max(kv_bytes(w) / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+        self._record("f2_mixed_single_launch", "pa_mixed_attention",
+                     "mixed iteration decode + prefill in one call (the two rows above)", ms,
+                     kv_bytes(w), "GB/s", HBM_PEAK_GBS, "hbm",
+                     separate_us=round(sep, 2),
+                     speedup_vs_separate=round(sep / (ms[0] * 1e3), 3),
+                     roofline_us=round(bound_us * 1e6, 2),
+                     roofline_note="max(decode K+V bytes / 8 TB/s, prefill flops / 2.5 "
+                                   "PFLOP/s): the time if both parts ran at peak, fully "
+                                   "overlapped; frac counts the decode bytes only",
+                     frac_of_overlap_bound=round(bound_us * 1e6 / (ms[0] * 1e3), 4),
+                     prefill_flops=flops)
+        del d, w, pq, pout, out2, pout2
         return self.out
 
 

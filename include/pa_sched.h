@@ -151,8 +151,9 @@ int pa_sched_step(pa_sched* s, int32_t* buf, int64_t cap, int64_t* used);
 /*
  * The engine: a scheduler driving the kernels of include/pa.h on one stream.
  * Every iteration's packet goes host -> device with one asynchronous copy
- * from a pinned ring slot, then pa_copy_blocks, pa_append_kv,
- * pa_prefill_chunk and pa_decode are enqueued. There are no model weights:
+ * from a pinned ring slot, then pa_copy_blocks and pa_append_kv are
+ * enqueued, then the attention: pa_mixed_attention when the iteration has
+ * both prefill chunks and decodes, else pa_prefill_chunk or pa_decode. There are no model weights:
  * queries and new K/V rows come from caller buffers, row i of the
  * iteration's tokens (prefill tokens first, then decode tokens) reading row i
  * of k_rows / v_rows, prefill token i reading row i of q_prefill and decode i

@@ -449,6 +449,11 @@ struct pa_engine {
     if (int st = pa_append_kv(pool, k_rows, v_rows, slots, n_slots, c.num_blocks, hkv, d,
                               c.block_size, dtype, stream))
       return st;
+    if (n_chunks > 0 && n_dec > 0)  // both kinds of work: one fused launch
+      return pa_mixed_attention(out_decode, q_decode, dec_tab, dec_ctx, n_dec, mb, c.max_len,
+                                out_prefill, q_prefill, chunk_tab, chunk_ctx, qsl, n_chunks,
+                                n_pre, h[11], mb, pool, hq, hkv, d, c.block_size, c.num_blocks,
+                                scale, dtype, ws, ws_bytes, stream);
     if (n_chunks > 0) {
       if (int st = pa_prefill_chunk(out_prefill, q_prefill, pool, chunk_tab, chunk_ctx, qsl,
                                     n_chunks, n_pre, h[11], mb, hq, hkv, d, c.block_size,
