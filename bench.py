@@ -47,6 +47,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
+PCIE_PEAK_GBS = 64.0       # PCIe Gen5 x16, nominal per direction (host link of the swap row)
 METRIC = "paged decode attention: effective KV HBM GB/s (% of peak) and seq-layers/s"
 WORKLOAD_DESC = {
     "gqa": "GQA long-tail decode: 256 seqs, 64 q / 8 kv heads, head_dim 128, block_size 16, "
@@ -378,6 +379,34 @@ class Rows:
                      frac_of_overlap_bound=round(bound_us * 1e6 / (ms[0] * 1e3), 4),
                      prefill_flops=flops)
         del d, w, pq, pout, out2, pout2
+
+        # -- swap: 1024 blocks of 64 KiB out to pinned host memory and back ----------------
+        w = make_workload("gqa")
+        pool = to_dev(w.pool, w.dtype, self.torch)
+        E = w.block_elems
+        n = 1024
+        host = self.torch.empty(n * E, dtype=pool.dtype).pin_memory()
+        rng = np.random.default_rng(1)
+        src = rng.choice(w.num_blocks, n, replace=False).astype(np.int32)
+        out_pairs = i32(np.stack([src, np.arange(n, dtype=np.int32)], 1), self.torch)
+        in_pairs = i32(np.stack([np.arange(n, dtype=np.int32), src], 1), self.torch)
+        nbytes = float(n * E * w.elem_bytes)
+        for key, pairs, direction, what in (("f3_swap_out", out_pairs, pa.SWAP_OUT, "device -> host"),
+                                            ("f3_swap_in", in_pairs, pa.SWAP_IN, "host -> device")):
+            def swap(pairs=pairs, direction=direction):
+                pa.pa_swap_blocks(pool, host, pairs, direction, w.num_kv_heads, w.head_dim,
+                                  w.block_size)
+
+            ms = time_calls(swap, self.torch, self.repeats)
+            self._record(key, "pa_swap_blocks", f"{n} blocks of 64 KiB (64 MiB), {what}, "
+                         "pinned host memory", ms, nbytes, "GB/s", PCIE_PEAK_GBS, "host link",
+                         self._oracle(lambda: oracle.swap_blocks(w.pool[src], w.pool[src],
+                                                                 np.stack([np.arange(n)] * 2, 1),
+                                                                 0 if direction == 0 else 1),
+                                      nbytes / 1e9, "GB/s",
+                                      f"all {n} blocks, NumPy block copy, 1 thread"),
+                         peak_note="PCIe Gen5 x16 nominal, per direction")
+        del pool, host
         return self.out
 
 

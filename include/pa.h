@@ -81,7 +81,8 @@ enum {
   PA_ERR_WORKSPACE = 4,   /* workspace too small */
   PA_ERR_LAUNCH = 5,      /* the HIP launch failed */
   PA_ERR_ALIAS = 6,       /* output overlaps an input it must not overlap */
-  PA_ERR_ALIGN = 7        /* a data pointer is not 16-byte aligned */
+  PA_ERR_ALIGN = 7,       /* a data pointer is not 16-byte aligned */
+  PA_ERR_HOST = 8         /* host pool is not pinned, device-mapped host memory */
 };
 
 /* Tokens per split-K partition of pa_decode. A sequence of n tokens is cut at
@@ -187,6 +188,30 @@ int pa_prefill_chunk(void* out, const void* q, const void* kv_pool,
                      int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                      int32_t dtype, void* stream);
+
+enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 };
+
+/*
+ * pa_swap_blocks — move whole blocks between the device pool and a pool in
+ * pinned host memory. ("Module 4 · Batching, Scheduling, and Paging",
+ * section "PagedAttention": when HBM is exhausted a request is evicted, its
+ * KV swapped to CPU memory or dropped and recomputed later.)
+ *
+ *   host_pool       num_host_blocks blocks of the same size and layout as the
+ *                   device pool's, in pinned host memory that the device
+ *                   addresses directly (hipHostMalloc, or a pinned torch
+ *                   tensor); anything else returns PA_ERR_HOST.
+ *   block_pairs     device int32 [num_pairs][2] (src, dst):
+ *                   PA_SWAP_OUT copies device block src to host block dst,
+ *                   PA_SWAP_IN copies host block src to device block dst.
+ * Pairs must not write a block another pair of the call reads or writes.
+ * The copy is a kernel reading and writing the host pool over the host link;
+ * like every call it only enqueues on `stream`. Out-of-range ids are skipped.
+ */
+int pa_swap_blocks(void* kv_pool, void* host_pool, const int32_t* block_pairs, int32_t num_pairs,
+                   int32_t direction, int32_t num_blocks, int32_t num_host_blocks,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                   void* stream);
 
 /*
  * pa_mixed_attention — one iteration's decode batch and prefill chunks

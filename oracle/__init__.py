@@ -22,7 +22,8 @@ pure-Python brute force in ``oracle.brute``). No function here is unpinned.
 """
 from .paged_attention import (append, attend, attend_partitioned, check_slots, copy_blocks,
                               decode, decode_elements, gather, merge_partials, pool_views,
-                              prefill)
+                              prefill, swap_blocks)
 
 __all__ = ["append", "attend", "attend_partitioned", "check_slots", "copy_blocks", "decode",
-           "decode_elements", "gather", "merge_partials", "pool_views", "prefill"]
+           "decode_elements", "gather", "merge_partials", "pool_views", "prefill",
+           "swap_blocks"]

@@ -162,6 +162,23 @@ def copy_blocks(pool, pairs):
     return out
 
 
+def swap_blocks(pool, host, pairs, direction):
+    """New (pool, host) after moving whole blocks between them.
+
+    direction 0 (out): host[dst] = pool[src]; 1 (in): pool[dst] = host[src].
+    An evicted request's blocks go to CPU memory and come back later
+    ("Module 4", section "PagedAttention"). Reads see the state before the
+    call.
+    """
+    new_pool, new_host = pool.copy(), host.copy()
+    for src, dst in np.asarray(pairs).reshape(-1, 2):
+        if direction == 0:
+            new_host[int(dst)] = pool[int(src)]
+        else:
+            new_pool[int(dst)] = host[int(src)]
+    return new_pool, new_host
+
+
 def check_slots(slot_mapping, append_owner, block_tables, block_size,
                 prefill_block_tables=None) -> None:
     """Assert each slot equals the one its (table, row, position) implies.

@@ -18,9 +18,11 @@ import torch
 
 __all__ = ["PAError", "load", "lib_path", "pa_append_kv", "pa_copy_blocks", "pa_decode",
            "pa_decode_workspace_size", "pa_prefill_chunk", "pa_mixed_attention",
+           "pa_swap_blocks", "SWAP_OUT", "SWAP_IN",
            "pa_status_string", "new_decode_workspace", "DECODE_PARTITION"]
 
 DECODE_PARTITION = 512  # PA_DECODE_PARTITION in include/pa.h
+SWAP_OUT, SWAP_IN = 0, 1  # PA_SWAP_OUT, PA_SWAP_IN
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libpa.so"
@@ -68,6 +70,9 @@ def load() -> ctypes.CDLL:
                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_int, ctypes.c_float, _c_int, _c_ptr]
     lib.pa_prefill_chunk.restype = ctypes.c_int
+    lib.pa_swap_blocks.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   _c_int, _c_int, _c_int, _c_ptr]
+    lib.pa_swap_blocks.restype = ctypes.c_int
     lib.pa_mixed_attention.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int,
                                        _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
                                        _c_int, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
@@ -222,3 +227,24 @@ def pa_mixed_attention(dec_out, dec_q, dec_tables, dec_lens, max_context_len: in
         pmb, _dev(kv_pool, "kv_pool"), hq, num_kv_heads, d, block_size, nb, float(scale),
         _dtype_code(dec_q, kv_pool), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def pa_swap_blocks(kv_pool, host_pool, block_pairs, direction: int, num_kv_heads: int,
+                   head_dim: int, block_size: int, stream=None) -> None:
+    """Copy whole blocks between the device pool and a pinned host pool.
+
+    ``host_pool`` is a pinned CPU tensor of the pool's dtype holding whole
+    blocks; ``block_pairs`` [P][2] int32 on the device holds (src, dst):
+    device -> host for SWAP_OUT, host -> device for SWAP_IN.
+    """
+    if not isinstance(host_pool, torch.Tensor) or host_pool.device.type != "cpu":
+        raise ValueError("host_pool must be a CPU tensor")
+    if not host_pool.is_pinned() or not host_pool.is_contiguous():
+        raise ValueError("host_pool must be pinned and contiguous")
+    nb = _num_blocks(kv_pool, num_kv_heads, block_size, head_dim)
+    nh = _num_blocks(host_pool, num_kv_heads, block_size, head_dim)
+    P = block_pairs.shape[0] if block_pairs.numel() else 0
+    _check("pa_swap_blocks", load().pa_swap_blocks(
+        _dev(kv_pool, "kv_pool"), host_pool.data_ptr(),
+        _i32(block_pairs, "block_pairs") if P else None, P, int(direction), nb, nh,
+        num_kv_heads, head_dim, block_size, _dtype_code(kv_pool, host_pool), _stream(stream)))

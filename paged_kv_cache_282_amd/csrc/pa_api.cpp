@@ -184,6 +184,30 @@ int pa_prefill_chunk(void* out, const void* q, const void* kv_pool,
                                       scale, dtype, static_cast<hipStream_t>(stream)));
 }
 
+int pa_swap_blocks(void* kv_pool, void* host_pool, const int32_t* block_pairs, int32_t num_pairs,
+                   int32_t direction, int32_t num_blocks, int32_t num_host_blocks,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                   void* stream) {
+  if (num_pairs < 0 || num_host_blocks < 0) return PA_ERR_SHAPE;
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN) return PA_ERR_SHAPE;
+  if (int s = check_pool(num_blocks, num_kv_heads, head_dim, block_size, dtype)) return s;
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > 65535) return PA_ERR_SHAPE;  // grid.y limit
+  if (!kv_pool || !host_pool || !block_pairs) return PA_ERR_NULL;
+  if (!aligned16(kv_pool) || !aligned16(host_pool)) return PA_ERR_ALIGN;
+  // The host pool must be pinned memory the device can address; its device
+  // address is looked up (the same value under unified addressing).
+  void* host_dev = nullptr;
+  if (hipHostGetDevicePointer(&host_dev, host_pool, 0) != hipSuccess || !host_dev) {
+    (void)hipGetLastError();  // leave no error behind for a later launch check
+    return PA_ERR_HOST;
+  }
+  return status_of(pa::launch_swap(kv_pool, host_dev, block_pairs, num_pairs,
+                                   direction == PA_SWAP_OUT, num_host_blocks,
+                                   shape(num_blocks, num_kv_heads, head_dim, block_size), dtype,
+                                   static_cast<hipStream_t>(stream)));
+}
+
 int pa_mixed_attention(void* dec_out, const void* dec_q, const int32_t* dec_block_tables,
                        const int32_t* dec_context_lens, int32_t num_seqs,
                        int32_t dec_max_blocks_per_seq, int32_t max_context_len, void* pre_out,
@@ -242,6 +266,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_ALIAS: return "output overlaps an input";
     case PA_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
+    case PA_ERR_HOST: return "host pool is not pinned, device-mapped host memory";
     case PA_SCHED_FINISHED: return "every request has finished";
     case PA_ERR_STATE: return "scheduler invariant broken (a lone request does not fit, or no progress)";
     default: return "unknown status";

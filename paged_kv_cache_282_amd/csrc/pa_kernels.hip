@@ -1502,16 +1502,21 @@ __global__ __launch_bounds__(256) void append_kernel(T* __restrict__ pool,
   for (int e = 0; e < 8; ++e) vslice[4 * e + r] = v[e];
 }
 
-__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ pool,
+// Whole blocks from one pool to another (the same one for copy-on-write; the
+// device pool and a pinned host pool for swapping): pair p copies block
+// pairs[2p] of `from` onto block pairs[2p+1] of `to`.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(const uint8_t* __restrict__ from,
+                                                          uint8_t* __restrict__ to,
                                                           const int32_t* __restrict__ pairs,
-                                                          int64_t blk_bytes, int64_t nb) {
+                                                          int64_t blk_bytes, int64_t nb_from,
+                                                          int64_t nb_to) {
   const int pi = blockIdx.y;
   const int src = pairs[2 * pi], dst = pairs[2 * pi + 1];
-  if (static_cast<uint32_t>(src) >= static_cast<uint64_t>(nb) ||
-      static_cast<uint32_t>(dst) >= static_cast<uint64_t>(nb))
+  if (static_cast<uint32_t>(src) >= static_cast<uint64_t>(nb_from) ||
+      static_cast<uint32_t>(dst) >= static_cast<uint64_t>(nb_to))
     return;
-  const u32x4* s = reinterpret_cast<const u32x4*>(pool + src * blk_bytes);
-  u32x4* d = reinterpret_cast<u32x4*>(pool + dst * blk_bytes);
+  const u32x4* s = reinterpret_cast<const u32x4*>(from + src * blk_bytes);
+  u32x4* d = reinterpret_cast<u32x4*>(to + dst * blk_bytes);
   const int64_t n16 = blk_bytes / 16;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
   int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -1640,7 +1645,24 @@ hipError_t launch_copy(void* pool, const int32_t* pairs, int num_pairs, const Po
   int gx = static_cast<int>((n16 + 1023) / 1024);  // about 4 x 16 B per thread
   gx = gx < 1 ? 1 : gx;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, num_pairs), dim3(256), 0, st,
-                     static_cast<uint8_t*>(pool), pairs, blk_bytes, ps.num_blocks);
+                     static_cast<const uint8_t*>(pool), static_cast<uint8_t*>(pool), pairs,
+                     blk_bytes, ps.num_blocks, ps.num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap(void* pool, void* host_dev, const int32_t* pairs, int num_pairs,
+                       bool out, int64_t num_host_blocks, const PoolShape& ps, int dtype,
+                       hipStream_t st) {
+  if (num_pairs == 0) return hipSuccess;
+  const int64_t blk_bytes = ps.block_elems() * (dtype == 0 ? 4 : 2);
+  const int64_t n16 = blk_bytes / 16;
+  int gx = static_cast<int>((n16 + 1023) / 1024);
+  gx = gx < 1 ? 1 : gx;
+  const uint8_t* from = static_cast<const uint8_t*>(out ? pool : host_dev);
+  uint8_t* to = static_cast<uint8_t*>(out ? host_dev : pool);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, num_pairs), dim3(256), 0, st, from, to, pairs,
+                     blk_bytes, out ? ps.num_blocks : num_host_blocks,
+                     out ? num_host_blocks : ps.num_blocks);
   return hipGetLastError();
 }
 

@@ -54,6 +54,13 @@ hipError_t launch_append(void* pool, const void* k_new, const void* v_new, const
 hipError_t launch_copy(void* pool, const int32_t* pairs, int num_pairs, const PoolShape& ps,
                        int dtype, hipStream_t stream);
 
+// Whole blocks between the device pool and a device-mapped host pool: out
+// copies pool[pair.src] to host[pair.dst], in copies host[pair.src] to
+// pool[pair.dst].
+hipError_t launch_swap(void* pool, void* host_dev, const int32_t* pairs, int num_pairs, bool out,
+                       int64_t num_host_blocks, const PoolShape& ps, int dtype,
+                       hipStream_t stream);
+
 hipError_t launch_decode(void* out, const void* q, const void* pool, const int32_t* tables,
                          const int32_t* lens, int num_seqs, int max_blocks_per_seq,
                          int max_context_len, int num_q_heads, const PoolShape& ps, float scale,

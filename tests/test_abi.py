@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["pa_append_kv", "pa_copy_blocks", "pa_decode",
                             "pa_decode_workspace_size", "pa_prefill_chunk",
-                            "pa_mixed_attention", "pa_status_string"])
+                            "pa_mixed_attention", "pa_swap_blocks", "pa_status_string"])
 
 
 def test_runtime_header_declares_the_runtime():
@@ -54,7 +54,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in list(range(8)) + [64, 65]:
+    for code in list(range(9)) + [64, 65]:
         s = pa.pa_status_string(code)
         assert s and s != "unknown status"
     assert pa.pa_status_string(99) == "unknown status"
@@ -184,3 +184,16 @@ def test_mixed_validation(lib):
     assert call(pout=FAKE) == ALIAS                   # prefill output over the decode output
     assert call(pout=FAKE2) == ALIAS                  # prefill output over the decode query
     assert call(dq=ctypes.c_void_p(0x200000)) == ALIAS  # decode query over the prefill output
+
+
+def test_swap_validation(lib):
+    f = lib.pa_swap_blocks
+    # (pool, host, pairs, P, direction, nb, nh, hkv, d, bs, dtype, stream)
+    assert f(FAKE, FAKE2, FAKE, 0, 0, 10, 4, 2, 128, 16, BF16, None) == OK
+    assert f(FAKE, FAKE2, FAKE, -1, 0, 10, 4, 2, 128, 16, BF16, None) == SHAPE
+    assert f(FAKE, FAKE2, FAKE, 2, 2, 10, 4, 2, 128, 16, BF16, None) == SHAPE   # direction
+    assert f(FAKE, None, FAKE, 2, 0, 10, 4, 2, 128, 16, BF16, None) == NULL
+    assert f(FAKE, FAKE2, None, 2, 1, 10, 4, 2, 128, 16, BF16, None) == NULL
+    assert f(FAKE, ctypes.c_void_p(0x80000008), FAKE, 2, 0, 10, 4, 2, 128, 16, BF16,
+             None) == ALIGN
+    assert f(FAKE, FAKE2, FAKE, 2, 0, 10, 4, 2, 96, 16, BF16, None) == UNSUPPORTED

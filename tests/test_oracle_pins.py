@@ -161,6 +161,35 @@ def test_copy_blocks_snapshot_semantics():
     assert np.array_equal(sw[y].view(np.uint16), w.pool[x].view(np.uint16))
 
 
+def test_swap_blocks_moves_whole_blocks_and_round_trips():
+    """Swap out copies device blocks to host blocks flat index by flat index;
+    swapping back with the pairs reversed restores the pool exactly; blocks
+    no pair names are untouched on both sides."""
+    w = make_workload("tiny")
+    rng = np.random.default_rng(8)
+    nh = 6
+    host = np.full((nh, w.pool.shape[1]), np.nan, np.float32)
+    src = rng.choice(w.pool.shape[0] - 1, 4, replace=False)
+    dst = rng.choice(nh, 4, replace=False)
+    pairs = np.stack([src, dst], 1)
+    pool2, host2 = oracle.swap_blocks(w.pool, host, pairs, 0)
+    assert np.array_equal(pool2.view(np.uint32), w.pool.view(np.uint32))
+    E = w.pool.shape[1]
+    flat_pool, flat_host = list(w.pool.reshape(-1)), host.reshape(-1).copy()
+    for s_, d_ in pairs:   # element by element, by flat index
+        for e in range(E):
+            flat_host[d_ * E + e] = flat_pool[s_ * E + e]
+    assert np.array_equal(host2.reshape(-1).view(np.uint32), flat_host.view(np.uint32))
+    untouched = [j for j in range(nh) if j not in set(dst.tolist())]
+    assert np.isnan(host2[untouched]).all()
+    # back in, into blocks cleared to zero first
+    cleared = w.pool.copy()
+    cleared[src] = 0.0
+    pool3, host3 = oracle.swap_blocks(cleared, host2, pairs[:, ::-1], 1)
+    assert np.array_equal(pool3.view(np.uint32), w.pool.view(np.uint32))
+    assert np.array_equal(host3.view(np.uint32), host2.view(np.uint32))
+
+
 # -- Q3, Q4: closed forms --------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
