@@ -415,7 +415,8 @@ ENGINE_DESC = ("iteration-level serving loop (no model weights): 1024 requests a
                "clipped [1, 1536], 20% of requests with 4 parallel samples; 32 q / 8 kv heads, "
                "head_dim 128, block_size 16, bf16; pool 8192 blocks (512 MB); at most 256 "
                "running samples, 2048 tokens and 512-token prefill chunks per iteration, "
-               "max_len 2048 (reservation: 128 blocks per sample)")
+               "max_len 2048 (reservation: 128 blocks per sample); the paged policy also on "
+               "a 3072-block pool, evicting by recomputation or by swapping to pinned host memory")
 
 
 def engine_rows(pa, torch, oracle_on: bool) -> dict:
@@ -447,10 +448,15 @@ def engine_rows(pa, torch, oracle_on: bool) -> dict:
     scale = 1.0 / np.sqrt(D)
     want = sum(sum(o) for _, o, _ in reqs)
 
-    def run(policy, stream_reqs):
+    def run(policy, stream_reqs, num_blocks=None, host_blocks=0):
+        c = dict(cfg, num_blocks=num_blocks or cfg["num_blocks"], num_host_blocks=host_blocks)
         ws = pa.new_decode_workspace(S, HQ, D, cfg["max_len"])
-        sched = runtime.Scheduler(policy=policy, free_order=order, requests=stream_reqs, **cfg)
-        eng = runtime.Engine(sched, pool, HKV, qp, qd, k, v, outp, outd, ws, scale)
+        sched = runtime.Scheduler(policy=policy, requests=stream_reqs, **c,
+                                  free_order=order if num_blocks is None
+                                  else np.random.default_rng(282).permutation(num_blocks))
+        blk = 2 * HKV * cfg["block_size"] * D
+        eng = runtime.Engine(sched, pool[: c["num_blocks"] * blk], HKV, qp, qd, k, v, outp, outd,
+                             ws, scale)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         st = eng.run()
@@ -461,11 +467,17 @@ def engine_rows(pa, torch, oracle_on: bool) -> dict:
 
     run("paged", reqs[:64])   # first launches of every kernel, outside the timed runs
     out = {"workload": ENGINE_DESC, "output_tokens": want, "policies": {}}
-    for policy in ("paged", "reserve", "static"):
-        st, wall = run(policy, reqs)
+    # the paged policy again on a pool of 3072 blocks (192 MB), where it must
+    # evict: dropping and recomputing victims, or swapping them to 4096
+    # pinned host blocks (256 MB)
+    runs = [("paged", "paged", None, 0), ("reserve", "reserve", None, 0),
+            ("static", "static", None, 0), ("paged_3072_recompute", "paged", 3072, 0),
+            ("paged_3072_swap", "paged", 3072, 4096)]
+    for name, policy, nblk, hblk in runs:
+        st, wall = run(policy, reqs, nblk, hblk)
         kv = st["decode_context_tokens"] * 2 * HKV * D * 2
         it = st["iterations"]
-        out["policies"][policy] = {
+        out["policies"][name] = {
             "tokens_per_s": round(want / wall, 1), "wall_ms": round(wall * 1e3, 2),
             "iterations": it, "us_per_iteration": round(wall * 1e6 / it, 2),
             "host_us_per_iteration": round(st["host_us"] / it, 2),
@@ -474,11 +486,13 @@ def engine_rows(pa, torch, oracle_on: bool) -> dict:
             "mean_decodes_per_iteration": round(st["decode_tokens"] / it, 1),
             "generated": st["generated"], "evictions": st["evictions"],
             "copies": st["copies"], "prefill_tokens": st["prefill_tokens"],
+            "swapped_blocks": st["swapped_blocks"],
             "decode_kv_GBps": round(kv / wall / 1e9, 1),
             "decode_kv_frac_of_hbm_peak": round(kv / wall / 1e9 / HBM_PEAK_GBS, 4)}
-        log(f"  engine {policy:8s} {want / wall:10.0f} tok/s  {it:6d} iterations  "
+        log(f"  engine {name:20s} {want / wall:10.0f} tok/s  {it:6d} iterations  "
             f"{wall * 1e3:8.1f} ms  host {st['host_us'] / it:6.1f} us/iter  "
-            f"decode KV {kv / wall / 1e9:7.1f} GB/s  evictions {st['evictions']}")
+            f"decode KV {kv / wall / 1e9:7.1f} GB/s  evictions {st['evictions']}  "
+            f"swapped {st['swapped_blocks']}")
     pol = out["policies"]
     out["paged_vs_static"] = round(pol["paged"]["tokens_per_s"] / pol["static"]["tokens_per_s"], 2)
     out["reserve_vs_static"] = round(pol["reserve"]["tokens_per_s"]

@@ -64,6 +64,8 @@ typedef struct {
   int32_t max_chunk;  /* longest prefill chunk */
   int32_t max_len;    /* longest context a sample may reach: prompt + output - 1 */
   int32_t policy;     /* PA_POLICY_* */
+  int32_t num_host_blocks; /* PAGED only: host blocks for swapping evicted requests
+                              (0: an evicted request is dropped and recomputed) */
 } pa_sched_config;
 
 typedef struct pa_sched pa_sched;
@@ -107,8 +109,11 @@ int32_t pa_sched_num_free(const pa_sched* s);
  *      take this iteration — one block per decode sample whose last block is
  *      full or shared, plus the blocks of each continuing prefill chunk —
  *      the most recently admitted running request is evicted: its blocks are
- *      released and it goes back to the head of the queue, to restart from its
- *      prompt.
+ *      released and it goes back to the head of the queue. With host blocks
+ *      configured, a decoding victim whose distinct blocks fit the free host
+ *      blocks is swapped out (each distinct block, in sample then table order,
+ *      to the next free host block) and keeps its progress; otherwise it
+ *      restarts from its prompt.
  *   4. Decode: every unfinished sample of the running requests (admission
  *      order, then sample order) appends the KV of its last token, one slot
  *      (allocated when its last block is full; a shared block is copied
@@ -117,8 +122,11 @@ int32_t pa_sched_num_free(const pa_sched* s);
  *   5. Prefill: each running request still in prefill gets its next chunk of
  *      min(remaining prompt, max_chunk, budget left) tokens.
  *   6. Admission (not after an eviction; STATIC only when no batch was
- *      running at the start of the iteration): the head of the queue is
- *      admitted while it fits the free slots (its samples count from
+ *      running at the start of the iteration): a swapped head comes back when
+ *      its unfinished samples fit the free slots and its blocks the free
+ *      device blocks (one new block per host block, its samples sharing as
+ *      before, host blocks released in order; no prefill, no budget). Else the
+ *      head of the queue is admitted while it fits the free slots (its samples count from
  *      admission on), the budget (continuous policies only: a static batch is
  *      formed whole and its later members start prefill in later iterations),
  *      and the pool (PAGED: the blocks of its first chunk; reservation
@@ -133,14 +141,17 @@ int32_t pa_sched_num_free(const pa_sched* s);
  *   header [16]: 0 iteration, 1 tokens generated, 2 copies, 3 slots (tokens
  *     appended), 4 prefill tokens, 5 chunks, 6 decodes, 7 admitted,
  *     8 preempted, 9 finished, 10 MB = ceil(max_len/bs) (table row width),
- *     11 longest chunk, 12..15 zero;
+ *     11 longest chunk, 12 swap-outs, 13 swap-ins, 14..15 zero;
  *   then: copies [copies][2] (src, dst); slots [slots] (prefill tokens in
  *     chunk order, then decode tokens in decode order); chunk_req [chunks];
  *     chunk_qsl [chunks+1] (query start of each chunk, then the prefill token
  *     count); chunk_ctx [chunks] (context after the chunk); chunk_tables
  *     [chunks][MB]; dec_req [decodes]; dec_sample [decodes]; dec_ctx [decodes]
  *     (context after the append); dec_tables [decodes][MB]; admitted;
- *     preempted; finished (request ids). Table rows are zero-padded.
+ *     preempted; finished (request ids); swap_out [swap-outs][2] (device
+ *     block, host block); swap_in [swap-ins][2] (host block, device block).
+ *     Table rows are zero-padded. On the GPU the swap-outs run first, then
+ *     the swap-ins, then the copies, appends and attention.
  * `buf` may be NULL (the plan is applied but not written); otherwise `cap`
  * must be at least pa_sched_plan_capacity(). *used receives the words
  * written. Returns PA_OK, PA_SCHED_FINISHED (nothing planned), PA_ERR_NULL,
@@ -150,6 +161,8 @@ int pa_sched_step(pa_sched* s, int32_t* buf, int64_t cap, int64_t* used);
 
 /*
  * The engine: a scheduler driving the kernels of include/pa.h on one stream.
+ * With host blocks configured it also owns that many pinned host blocks and
+ * moves swapped blocks with pa_swap_blocks.
  * Every iteration's packet goes host -> device with one asynchronous copy
  * from a pinned ring slot, then pa_copy_blocks and pa_append_kv are
  * enqueued, then the attention: pa_mixed_attention when the iteration has
@@ -181,6 +194,7 @@ typedef struct {
   int64_t decode_context_tokens; /* sum of the decodes' context lengths (tokens attended) */
   int64_t copies;
   int64_t evictions;
+  int64_t swapped_blocks; /* blocks swapped out (each comes back in once) */
   double host_us;         /* host time spent planning and enqueueing */
   double wait_us;         /* host time spent waiting for a ring slot (the device is behind) */
 } pa_engine_stats;

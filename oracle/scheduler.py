@@ -47,7 +47,18 @@ the design notes):
   * reservation (Orca, and static batching) holds ceil(max_len / bs) blocks per
     sample from admission until that sample finishes (static: until the batch
     ends); without paging, samples do not share, so the prompt's blocks are
-    copied into each further sample's reservation before its first decode.
+    copied into each further sample's reservation before its first decode;
+  * swapping (paged, when host blocks are configured): an evicted request that
+    is decoding and whose blocks fit the free host blocks is swapped out
+    instead of dropped -- each of its distinct blocks goes to one host block
+    (first appearance in sample, then table order; host blocks are a stack
+    like the device ones) -- and keeps its progress. Back at the head of the
+    queue it is swapped in when its samples fit the free slots and its blocks
+    the free device blocks: one new device block per host block, the samples'
+    sharing kept, the host blocks released in the same order. A swapped-in
+    request needs no prefill and takes no token budget; it decodes from the
+    next iteration on. In one iteration the GPU runs the swap-outs, then the
+    swap-ins, then the copies, appends and attention.
 """
 from __future__ import annotations
 
@@ -66,6 +77,7 @@ class SchedConfig:
     max_chunk: int     # longest prefill chunk
     max_len: int       # longest context a sample may reach (prompt + output - 1)
     policy: str = "paged"
+    num_host_blocks: int = 0   # paged: host blocks for swapping (0: evictions recompute)
 
 
 @dataclass
@@ -80,6 +92,8 @@ class Plan:
     preempted: list = field(default_factory=list)
     finished: list = field(default_factory=list)
     generated: int = 0
+    swap_out: list = field(default_factory=list)  # (device block, host block), first
+    swap_in: list = field(default_factory=list)   # (host block, device block), second
 
 
 class _Sample:
@@ -90,6 +104,7 @@ class _Sample:
         self.out = out
         self.done = out == 1
         self.released = False
+        self.host_table = None  # host blocks while swapped out
 
 
 class _Request:
@@ -127,12 +142,15 @@ class Scheduler:
     def __init__(self, cfg: SchedConfig, free_order, requests):
         if cfg.policy not in POLICIES:
             raise ValueError(f"unknown policy {cfg.policy!r}")
+        if cfg.num_host_blocks < 0 or (cfg.num_host_blocks > 0 and cfg.policy != "paged"):
+            raise ValueError("host blocks serve the paged policy's evictions only")
         self.cfg = cfg
         order = [int(b) for b in free_order]
         if sorted(order) != list(range(cfg.num_blocks)):
             raise ValueError("free_order must list every block id once")
         self.free = order[::-1]               # a stack: free[-1] is taken next
         self.ref = [0] * cfg.num_blocks
+        self.host_free = list(range(cfg.num_host_blocks))[::-1]   # host block 0 first
         self.reqs = []
         for i, (p, outs, arr) in enumerate(requests):
             r = _Request(i, p, outs, arr)
@@ -180,8 +198,60 @@ class Scheduler:
         return table[j] * bs + pos % bs
 
     # -- eviction ----------------------------------------------------------------------
+    def _swap_out(self, r, plan):
+        """Swap a decoding request's blocks to host blocks; False if they do not fit."""
+        live = [q for q in r.samples if not q.released]
+        uniq = []
+        for q in live:
+            for b in q.table:
+                if b not in uniq:
+                    uniq.append(b)
+        if len(uniq) > len(self.host_free):
+            return False
+        where = {}
+        for b in uniq:
+            where[b] = self.host_free.pop()
+            plan.swap_out.append((b, where[b]))
+        for q in live:
+            q.host_table = [where[b] for b in q.table]
+            self._release_table(q.table)
+            q.table = None
+            self.slots_used -= 1
+        r.state = "swapped"
+        return True
+
+    def _swap_in(self, r, plan):
+        live = [q for q in r.samples if not q.released]
+        uniq = []
+        for q in live:
+            for h in q.host_table:
+                if h not in uniq:
+                    uniq.append(h)
+        if self.slots_used + len(live) > self.cfg.max_seqs or len(uniq) > len(self.free):
+            return False
+        where = {}
+        for h in uniq:
+            where[h] = self._alloc()
+            plan.swap_in.append((h, where[h]))
+        for q in live:
+            q.table = [where[h] for h in q.host_table]
+            q.host_table = None
+        for b in where.values():   # the samples share blocks as before
+            self.ref[b] = sum(q.table.count(b) for q in live)
+        for h in uniq:
+            self.host_free.append(h)
+        self.slots_used += len(live)
+        r.state = "decode"
+        return True
+
     def _evict(self, rid, plan):
         r = self.reqs[rid]
+        if r.state == "decode" and self.cfg.num_host_blocks > 0 and self._swap_out(r, plan):
+            r.evictions += 1
+            self.running.remove(rid)
+            self.waiting.appendleft(rid)
+            plan.preempted.append(rid)
+            return
         if r.state == "prefill":
             self._release_table(r.table)
             for t in r.reserved:
@@ -297,6 +367,13 @@ class Scheduler:
         while admitting and self.waiting and (budget > 0 or cfg.policy == "static"):
             rid = self.waiting[0]
             r = self.reqs[rid]
+            if r.state == "swapped":   # back in, with its progress
+                if not self._swap_in(r, plan):
+                    break
+                self.waiting.popleft()
+                self.running.append(rid)
+                plan.admitted.append(rid)
+                continue
             if self.slots_used + r.n > cfg.max_seqs:
                 break
             if cfg.policy == "paged":
@@ -343,7 +420,8 @@ class Scheduler:
                     self.running.remove(rid)
                     plan.finished.append(rid)
         self.it += 1
-        if not (plan.slots or plan.copies or plan.preempted or plan.finished) and not self.pending:
+        if not (plan.slots or plan.copies or plan.preempted or plan.finished or plan.swap_in) \
+                and not self.pending:
             # nothing ran and nothing is yet to arrive: with the pool whole and
             # every request fitting alone, this cannot happen
             raise AssertionError(f"iteration {plan.iteration} made no progress")

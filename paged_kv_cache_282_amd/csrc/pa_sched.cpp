@@ -49,13 +49,14 @@ class BlockPool {
 
 struct Seq {  // one sample after its prompt is cached
   std::vector<int32_t> table;
+  std::vector<int32_t> host_table;  // its blocks' host copies while swapped out
   int32_t cached = 0;  // tokens whose KV is in the pool
   int32_t made = 0;    // tokens generated
   int32_t want = 0;
   bool finished = false, released = false;
 };
 
-enum class Phase { kQueued, kPrefill, kDecode, kDone };
+enum class Phase { kQueued, kPrefill, kDecode, kSwapped, kDone };
 
 struct Req {
   int32_t prompt = 0, arrival = 0;
@@ -81,12 +82,13 @@ struct PlanBuf {
   std::vector<int32_t> chunk_req, chunk_start, chunk_ctx, chunk_tab;
   std::vector<int32_t> dec_req, dec_sample, dec_ctx, dec_tab;
   std::vector<int32_t> admitted, preempted, finished;
+  std::vector<int32_t> swap_out, swap_in;  // (device, host) and (host, device) pairs
   void reset(int32_t it) {
     iteration = it;
     generated = longest_chunk = 0;
     for (auto* v : {&copies, &pre_slots, &dec_slots, &chunk_req, &chunk_start, &chunk_ctx,
                     &chunk_tab, &dec_req, &dec_sample, &dec_ctx, &dec_tab, &admitted,
-                    &preempted, &finished})
+                    &preempted, &finished, &swap_out, &swap_in})
       v->clear();
   }
 };
@@ -103,6 +105,7 @@ struct pa_sched {
   std::vector<int32_t> running;  // admission order
   int32_t slots_used = 0;
   std::vector<int32_t> owed_copies;
+  std::vector<int32_t> host_free;  // stack of host blocks for swapped requests
   int32_t iteration = 0;
   PlanBuf plan;
 
@@ -161,8 +164,86 @@ struct pa_sched {
     return want;
   }
 
+  // Distinct entries of the tables of the unreleased samples, in sample then
+  // table order.
+  template <typename Get>
+  std::vector<int32_t> distinct(const Req& r, Get get) const {
+    std::vector<int32_t> seen;
+    for (const Seq& q : r.seqs) {
+      if (q.released) continue;
+      for (int32_t b : get(q))
+        if (std::find(seen.begin(), seen.end(), b) == seen.end()) seen.push_back(b);
+    }
+    return seen;
+  }
+
+  // A decoding request's blocks to host blocks; false if they do not fit.
+  bool swap_out(Req& r) {
+    const std::vector<int32_t> blocks = distinct(r, [](const Seq& q) { return q.table; });
+    if (blocks.size() > host_free.size()) return false;
+    std::vector<int32_t> host(blocks.size());
+    for (size_t i = 0; i < blocks.size(); ++i) {
+      host[i] = host_free.back();
+      host_free.pop_back();
+      plan.swap_out.push_back(blocks[i]);
+      plan.swap_out.push_back(host[i]);
+    }
+    for (Seq& q : r.seqs) {
+      if (q.released) continue;
+      q.host_table.clear();
+      for (int32_t b : q.table)
+        q.host_table.push_back(host[std::find(blocks.begin(), blocks.end(), b) - blocks.begin()]);
+      pool.drop_all(q.table);
+      q.table.clear();
+      --slots_used;
+    }
+    r.phase = Phase::kSwapped;
+    return true;
+  }
+
+  // A swapped request back onto the device; false if it does not fit yet.
+  bool swap_in(Req& r) {
+    int32_t live = 0;
+    for (const Seq& q : r.seqs) live += q.released ? 0 : 1;
+    const std::vector<int32_t> host = distinct(r, [](const Seq& q) { return q.host_table; });
+    if (slots_used + live > cfg.max_seqs ||
+        static_cast<int64_t>(host.size()) > pool.free_count())
+      return false;
+    std::vector<int32_t> dev(host.size());
+    for (size_t i = 0; i < host.size(); ++i) {
+      dev[i] = pool.take();
+      plan.swap_in.push_back(host[i]);
+      plan.swap_in.push_back(dev[i]);
+    }
+    for (Seq& q : r.seqs) {
+      if (q.released) continue;
+      q.table.clear();
+      for (int32_t h : q.host_table)
+        q.table.push_back(dev[std::find(host.begin(), host.end(), h) - host.begin()]);
+      q.host_table.clear();
+    }
+    // take() counted one user per block; every further table use adds one
+    std::vector<int32_t> uses(host.size(), 0);
+    for (const Seq& q : r.seqs) {
+      if (q.released) continue;
+      for (int32_t b : q.table) ++uses[std::find(dev.begin(), dev.end(), b) - dev.begin()];
+    }
+    for (size_t i = 0; i < dev.size(); ++i)
+      for (int32_t u = 1; u < uses[i]; ++u) pool.share(dev[i]);
+    for (int32_t h : host) host_free.push_back(h);
+    slots_used += live;
+    r.phase = Phase::kDecode;
+    return true;
+  }
+
   void evict(int32_t rid) {
     Req& r = reqs[rid];
+    if (r.phase == Phase::kDecode && cfg.num_host_blocks > 0 && swap_out(r)) {
+      running.erase(std::find(running.begin(), running.end(), rid));
+      queue.push_front(rid);
+      plan.preempted.push_back(rid);
+      return;
+    }
     if (r.phase == Phase::kPrefill) {
       pool.drop_all(r.prompt_table);
       for (auto& t : r.spare) pool.drop_all(t);
@@ -333,14 +414,25 @@ struct pa_sched {
     // A static batch is formed whole; continuous batching admits only what the
     // budget can start on this iteration.
     const bool whole_batch = cfg.policy == PA_POLICY_STATIC;
-    while (may_admit && !queue.empty() && (budget > 0 || whole_batch) && admit_head(budget))
+    while (may_admit && !queue.empty() && (budget > 0 || whole_batch)) {
+      const int32_t head = queue.front();
+      if (reqs[head].phase == Phase::kSwapped) {  // back with its progress, no prefill
+        if (!swap_in(reqs[head])) break;
+        queue.pop_front();
+        running.push_back(head);
+        plan.admitted.push_back(head);
+        continue;
+      }
+      if (!admit_head(budget)) break;
       budget -= prefill_chunk(running.back(), budget);
+    }
     release_finished();
     ++iteration;
     // An iteration with no work while nothing is yet to arrive means the state
     // is broken (a whole pool always admits the head of the queue).
     if (plan.pre_slots.empty() && plan.dec_slots.empty() && plan.copies.empty() &&
-        plan.preempted.empty() && plan.finished.empty() && next_arrival == reqs.size())
+        plan.preempted.empty() && plan.finished.empty() && plan.swap_in.empty() &&
+        next_arrival == reqs.size())
       return PA_ERR_STATE;
     return PA_OK;
   }
@@ -348,7 +440,9 @@ struct pa_sched {
   int64_t capacity() const {
     const int64_t seqs = cfg.max_seqs;
     const int64_t copies = 2 * (seqs * mb + seqs);
-    return kHeader + copies + cfg.max_tokens + seqs * (3 + mb) + 1 + seqs * (3 + mb) + 3 * seqs;
+    const int64_t swaps = 4 * static_cast<int64_t>(cfg.num_blocks);
+    return kHeader + copies + cfg.max_tokens + seqs * (3 + mb) + 1 + seqs * (3 + mb) + 3 * seqs +
+           swaps;
   }
 
   int64_t words() const {
@@ -357,7 +451,8 @@ struct pa_sched {
                                           p.dec_slots.size() + 3 * p.chunk_req.size() + 1 +
                                           p.chunk_tab.size() + 3 * p.dec_req.size() +
                                           p.dec_tab.size() + p.admitted.size() +
-                                          p.preempted.size() + p.finished.size());
+                                          p.preempted.size() + p.finished.size() +
+                                          p.swap_out.size() + p.swap_in.size());
   }
 
   void write(int32_t* buf) const {
@@ -376,6 +471,8 @@ struct pa_sched {
     h[9] = static_cast<int32_t>(p.finished.size());
     h[10] = mb;
     h[11] = p.longest_chunk;
+    h[12] = static_cast<int32_t>(p.swap_out.size() / 2);
+    h[13] = static_cast<int32_t>(p.swap_in.size() / 2);
     int32_t* w = buf + kHeader;
     auto put = [&w](const std::vector<int32_t>& v) { w = std::copy(v.begin(), v.end(), w); };
     put(p.copies);
@@ -393,6 +490,8 @@ struct pa_sched {
     put(p.admitted);
     put(p.preempted);
     put(p.finished);
+    put(p.swap_out);
+    put(p.swap_in);
   }
 };
 
@@ -414,6 +513,7 @@ struct pa_engine {
   hipStream_t stream = nullptr;
   int64_t cap = 0;
   int32_t* host_ring = nullptr;  // pinned, kRing packets
+  void* host_pool = nullptr;     // pinned, the scheduler's host blocks for swapping
   int32_t* dev_ring = nullptr;
   hipEvent_t sent[kRing] = {};
   bool used[kRing] = {};
@@ -424,6 +524,7 @@ struct pa_engine {
     for (auto& e : sent)
       if (e) (void)hipEventDestroy(e);
     if (host_ring) (void)hipHostFree(host_ring);
+    if (host_pool) (void)hipHostFree(host_pool);
     if (dev_ring) (void)hipFree(dev_ring);
   }
 
@@ -440,6 +541,17 @@ struct pa_engine {
     const int32_t* dec_req = chunk_tab + static_cast<int64_t>(n_chunks) * mb;
     const int32_t* dec_ctx = dec_req + 2 * n_dec;
     const int32_t* dec_tab = dec_ctx + n_dec;
+    const int32_t* swap_out = dec_tab + static_cast<int64_t>(n_dec) * mb + h[7] + h[8] + h[9];
+    const int32_t* swap_in = swap_out + 2 * h[12];
+    // blocks leave before any is reused, and return before anything is written
+    if (h[12] > 0)
+      if (int st = pa_swap_blocks(pool, host_pool, swap_out, h[12], PA_SWAP_OUT, c.num_blocks,
+                                  c.num_host_blocks, hkv, d, c.block_size, dtype, stream))
+        return st;
+    if (h[13] > 0)
+      if (int st = pa_swap_blocks(pool, host_pool, swap_in, h[13], PA_SWAP_IN, c.num_blocks,
+                                  c.num_host_blocks, hkv, d, c.block_size, dtype, stream))
+        return st;
     for (int32_t i = 0; i < n_copies; i += 65535) {
       const int32_t n = std::min(65535, n_copies - i);
       if (int st = pa_copy_blocks(pool, copies + 2 * i, n, c.num_blocks, hkv, d, c.block_size,
@@ -499,6 +611,7 @@ struct pa_engine {
     for (int32_t ctx : s->plan.dec_ctx) stats.decode_context_tokens += ctx;
     stats.copies += h[2];
     stats.evictions += h[8];
+    stats.swapped_blocks += h[12];
     const auto t3 = clock::now();
     using us = std::chrono::duration<double, std::micro>;
     stats.host_us += us(t1 - t0).count() + us(t3 - t2).count();
@@ -519,7 +632,8 @@ int pa_sched_create(const pa_sched_config* cfg, const int32_t* free_order, int32
   const pa_sched_config& c = *cfg;
   if (c.num_blocks <= 0 || c.block_size <= 0 || c.max_seqs <= 0 || c.max_tokens <= 0 ||
       c.max_chunk <= 0 || c.max_len <= 0 || num_requests < 0 || c.policy < PA_POLICY_PAGED ||
-      c.policy > PA_POLICY_STATIC)
+      c.policy > PA_POLICY_STATIC || c.num_host_blocks < 0 ||
+      (c.num_host_blocks > 0 && c.policy != PA_POLICY_PAGED))
     return PA_ERR_SHAPE;
   std::vector<char> seen(c.num_blocks, 0);
   for (int32_t i = 0; i < c.num_blocks; ++i) {
@@ -531,6 +645,7 @@ int pa_sched_create(const pa_sched_config* cfg, const int32_t* free_order, int32
   s->cfg = c;
   s->mb = cdiv(c.max_len, c.block_size);
   s->pool.init(free_order, c.num_blocks);
+  for (int32_t h = c.num_host_blocks - 1; h >= 0; --h) s->host_free.push_back(h);
   s->reqs.resize(num_requests);
   for (int32_t r = 0; r < num_requests; ++r) {
     Req& q = s->reqs[r];
@@ -611,6 +726,12 @@ int pa_engine_create(pa_sched* s, void* kv_pool, int32_t num_kv_heads, int32_t n
             hipMalloc(reinterpret_cast<void**>(&e->dev_ring), bytes) == hipSuccess;
   for (auto& ev : e->sent)
     ok = ok && hipEventCreateWithFlags(&ev, hipEventDisableTiming) == hipSuccess;
+  if (ok && s->cfg.num_host_blocks > 0) {
+    const size_t blk = size_t(2) * num_kv_heads * s->cfg.block_size * head_dim *
+                       (dtype == PA_F32 ? 4 : 2);
+    ok = hipHostMalloc(&e->host_pool, blk * s->cfg.num_host_blocks, hipHostMallocDefault) ==
+         hipSuccess;
+  }
   if (!ok) {
     delete e;
     return PA_ERR_LAUNCH;

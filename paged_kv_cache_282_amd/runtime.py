@@ -23,13 +23,13 @@ _i64 = ctypes.c_int64
 
 class _Config(ctypes.Structure):
     _fields_ = [("num_blocks", _i), ("block_size", _i), ("max_seqs", _i), ("max_tokens", _i),
-                ("max_chunk", _i), ("max_len", _i), ("policy", _i)]
+                ("max_chunk", _i), ("max_len", _i), ("policy", _i), ("num_host_blocks", _i)]
 
 
 class EngineStats(ctypes.Structure):
     _fields_ = [("iterations", _i64), ("generated", _i64), ("prefill_tokens", _i64),
                 ("decode_tokens", _i64), ("decode_context_tokens", _i64), ("copies", _i64),
-                ("evictions", _i64),
+                ("evictions", _i64), ("swapped_blocks", _i64),
                 ("host_us", ctypes.c_double), ("wait_us", ctypes.c_double)]
 
     def as_dict(self):
@@ -70,7 +70,7 @@ def _arr(x):
 def parse_plan(buf: np.ndarray) -> dict:
     """Decode one plan packet (int32 words) into lists."""
     h = [int(v) for v in buf[:16]]
-    it, gen, nc, ns, npre, nch, nd, na, npr, nf, mb, longest = h[:12]
+    it, gen, nc, ns, npre, nch, nd, na, npr, nf, mb, longest, nso, nsi = h[:14]
     w = 16
 
     def take(n):
@@ -94,6 +94,8 @@ def parse_plan(buf: np.ndarray) -> dict:
                    for c in range(nch)],
         "decodes": [(dreq[i], dsmp[i], dctx[i], dtab[i * mb:(i + 1) * mb]) for i in range(nd)],
         "admitted": take(na), "preempted": take(npr), "finished": take(nf),
+        "swap_out": [tuple(x) for x in np.asarray(take(2 * nso)).reshape(-1, 2).tolist()],
+        "swap_in": [tuple(x) for x in np.asarray(take(2 * nsi)).reshape(-1, 2).tolist()],
     }
 
 
@@ -101,10 +103,10 @@ class Scheduler:
     """The C++ scheduler. ``requests``: (prompt_len, [output_len per sample], arrival)."""
 
     def __init__(self, num_blocks, block_size, max_seqs, max_tokens, max_chunk, max_len,
-                 policy, free_order, requests):
+                 policy, free_order, requests, num_host_blocks=0):
         self._lib = _lib()
         cfg = _Config(num_blocks, block_size, max_seqs, max_tokens, max_chunk, max_len,
-                      POLICIES[policy])
+                      POLICIES[policy], num_host_blocks)
         prompts = _arr([r[0] for r in requests])
         arrival = _arr([r[2] for r in requests])
         offs = _arr(np.concatenate([[0], np.cumsum([len(r[1]) for r in requests])]))

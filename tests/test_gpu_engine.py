@@ -39,13 +39,16 @@ def _nan_pool(nb, dtype):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("policy,dtype", [("paged", "bf16"), ("paged", "f32"),
-                                          ("reserve", "bf16"), ("static", "f32")])
-def test_engine_matches_the_oracle_every_iteration(policy, dtype):
-    print(f"\nengine parity: policy={policy} dtype={dtype}", flush=True)
+@pytest.mark.parametrize("policy,dtype,host_blocks", [("paged", "bf16", 0), ("paged", "f32", 0),
+                                                      ("paged", "bf16", 24),
+                                                      ("reserve", "bf16", 0),
+                                                      ("static", "f32", 0)])
+def test_engine_matches_the_oracle_every_iteration(policy, dtype, host_blocks):
+    print(f"\nengine parity: policy={policy} dtype={dtype} host blocks={host_blocks}",
+          flush=True)
     # 20 blocks of 16 tokens: tight enough that the paged policy evicts
     cfg = dict(num_blocks=20, block_size=BS, max_seqs=6, max_tokens=48, max_chunk=32,
-               max_len=128)
+               max_len=128, num_host_blocks=host_blocks)
     reqs = make_request_stream(21, 14, prompt=(1, 70), output=(1, 40), multi_frac=0.3,
                                samples=2, arrival_every=2)
     order = np.random.default_rng(2).permutation(cfg["num_blocks"])
@@ -58,15 +61,17 @@ def test_engine_matches_the_oracle_every_iteration(policy, dtype):
     qp_raw = normal_values(ss[2], T * HQ * D, dtype).reshape(T, HQ, D)
     qd_raw = normal_values(ss[3], S * HQ * D, dtype).reshape(S, HQ, D)
     ref = _nan_pool(cfg["num_blocks"], dtype)
+    href = _nan_pool(max(host_blocks, 1), dtype)   # the oracle's host blocks
 
     pool = to_dev(ref, dtype)
     k, v, qp, qd = (to_dev(a, dtype) for a in (k_raw, v_raw, qp_raw, qd_raw))
     outp, outd = torch.zeros_like(qp), torch.zeros_like(qd)
     ws = pa.new_decode_workspace(S, HQ, D, cfg["max_len"])
     sched = runtime.Scheduler(policy=policy, free_order=order, requests=reqs, **cfg)
+    scfg = dict(cfg)
     eng = runtime.Engine(sched, pool, HKV, qp, qd, k, v, outp, outd, ws, scale)
-    osched = OracleScheduler(SchedConfig(policy=policy, **cfg), order, reqs)
-    n_dec = n_pre = n_copies = n_evict = 0
+    osched = OracleScheduler(SchedConfig(policy=policy, **scfg), order, reqs)
+    n_dec = n_pre = n_copies = n_evict = n_swap = 0
     while True:
         got = eng.step()
         want = osched.step()
@@ -80,8 +85,15 @@ def test_engine_matches_the_oracle_every_iteration(policy, dtype):
             [(r, q0, L, ctx, _padded(t, mb)) for r, q0, L, ctx, t in want.chunks], it
         assert [tuple(x) for x in got["decodes"]] == \
             [(r, s, ctx, _padded(t, mb)) for r, s, ctx, t in want.decodes], it
+        assert got["swap_out"] == [tuple(x) for x in want.swap_out], it
+        assert got["swap_in"] == [tuple(x) for x in want.swap_in], it
         torch.cuda.synchronize()
-        # the oracle's own pool after this iteration's copies and appends
+        # the oracle's own pool after this iteration's swaps, copies and appends
+        if want.swap_out:
+            ref, href = oracle.swap_blocks(ref, href, np.asarray(want.swap_out), 0)
+        if want.swap_in:
+            ref, href = oracle.swap_blocks(ref, href, np.asarray(want.swap_in), 1)
+        n_swap += len(want.swap_out)
         if want.copies:
             ref = oracle.copy_blocks(ref, np.asarray(want.copies, np.int64))
         nt = len(want.slots)
@@ -111,6 +123,7 @@ def test_engine_matches_the_oracle_every_iteration(policy, dtype):
     assert sched.num_free() == cfg["num_blocks"]
     assert n_dec > 0 and n_pre > 0 and n_copies > 0
     assert n_evict > 0 or policy != "paged"
+    assert n_swap > 0 or host_blocks == 0
     print(f"  {osched.it} iterations, {n_pre} prefill tokens, {n_dec} decodes, "
           f"{n_copies} copies", flush=True)
 

@@ -50,6 +50,8 @@ SCHED_MUTATIONS = {
     "fork_without_reference": ("                    for b in r.table:\n                        self.ref[b] += 1\n",
                                ""),
     "prefill_token_not_counted": ("self.gen = 1 ", "self.gen = 0 "),
+    "swap_in_forgets_sharing": ("self.ref[b] = sum(q.table.count(b) for q in live)", "pass"),
+    "swap_out_skips_host_order": ("where[b] = self.host_free.pop()", "where[b] = self.host_free.pop(0)"),
 }
 
 

@@ -227,3 +227,62 @@ def test_rejects_what_can_never_fit():
         Scheduler(cfg, range(4), [(4, [1, 1, 1], 0)])   # 3 samples > 2 slots
     with pytest.raises(ValueError):
         Scheduler(cfg, [0, 1, 2, 2], [(4, [1], 0)])     # not a permutation
+
+
+def test_hand_derived_swap_trace():
+    # bs 4, blocks handed out 0, 1, 2, ...; six host blocks, handed out 0, 1, ...
+    # Three requests, prompt 9, 12 tokens each. A and B are admitted (blocks
+    # 0-2 and 3-5); C does not fit. At position 12 A takes 6 and B takes 7. At
+    # position 16 (iteration 8) both need a block and none is free, so B, the
+    # latest admission, is swapped out: its distinct blocks 3, 4, 5, 7 go to
+    # host blocks 0..3, and A takes block 7 (released last). B cannot come
+    # back while A runs (4 blocks needed, 3 free), and C waits behind it.
+    # A finishes at iteration 11 (blocks 0, 1, 2, 6, 7 released in that
+    # order); at iteration 12 B returns into 7, 6, 2, 1 (the stack's top),
+    # keeping its 16 cached tokens, and C is admitted into 0, 5, 4. At
+    # iteration 13 B writes position 16, which opens a fifth block: 3.
+    cfg = SchedConfig(num_blocks=8, block_size=4, max_seqs=3, max_tokens=30, max_chunk=9,
+                      max_len=20, policy="paged", num_host_blocks=6)
+    s = Scheduler(cfg, list(range(8)), [(9, [12], 0), (9, [12], 0), (9, [12], 0)])
+    plans = _run(s, limit=200)
+    p8, p12 = plans[8], plans[12]
+    assert p8.preempted == [1]
+    assert p8.swap_out == [(3, 0), (4, 1), (5, 2), (7, 3)]
+    assert p8.decodes == [(0, 0, 17, [0, 1, 2, 6, 7])]
+    assert all(not p.admitted and not p.swap_in for p in plans[9:12])
+    assert plans[11].finished == [0]
+    assert p12.admitted == [1, 2]
+    assert p12.swap_in == [(0, 7), (1, 6), (2, 2), (3, 1)]
+    assert p12.chunks == [(2, 0, 9, 9, [0, 5, 4])]
+    assert plans[13].decodes[0] == (1, 0, 17, [7, 6, 2, 1, 3])   # B resumes at position 16
+    # nothing was recomputed
+    assert sum(p.generated for p in plans) == 36
+    assert sorted(s.host_free) == list(range(6))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_swapping_keeps_progress_and_returns_every_block(seed):
+    reqs = make_request_stream(seed, 40, prompt=(1, 60), output=(1, 90), multi_frac=0.3,
+                               samples=3, arrival_every=1)
+    cfg = SchedConfig(num_blocks=60, block_size=8, max_seqs=12, max_tokens=64, max_chunk=32,
+                      max_len=160, policy="paged", num_host_blocks=64)
+    s = Scheduler(cfg, np.random.default_rng(seed).permutation(60), reqs)
+    plans = _run(s)
+    outs = sum(len(p.swap_out) for p in plans)
+    assert outs > 0 and outs == sum(len(p.swap_in) for p in plans)
+    # every decoding victim was swapped (64 host blocks hold any request), so
+    # no token was generated twice (victims still in prefill restart it)
+    assert sum(p.generated for p in plans) == sum(sum(o) for _, o, _ in reqs)
+    # a swapped-in block receives exactly one host block, and a host block is
+    # read back before it is handed out again
+    held = {}
+    for p in plans:
+        for b, h in p.swap_out:
+            assert h not in held
+            held[h] = b
+        for h, b in p.swap_in:
+            assert h in held
+            del held[h]
+    assert not held
+    _check_invariants(s, plans, reqs, 8)
+    assert sorted(s.host_free) == list(range(64))

@@ -35,6 +35,7 @@ def oracle_packets(cfg: dict, policy, order, reqs):
             "chunks": [(r, q0, L, ctx, _padded(t, mb)) for r, q0, L, ctx, t in p.chunks],
             "decodes": [(r, k, ctx, _padded(t, mb)) for r, k, ctx, t in p.decodes],
             "admitted": p.admitted, "preempted": p.preempted, "finished": p.finished,
+            "swap_out": [tuple(x) for x in p.swap_out], "swap_in": [tuple(x) for x in p.swap_in],
         })
     return out
 
@@ -47,7 +48,8 @@ def native_packets(cfg: dict, policy, order, reqs):
         p["chunks"] = [tuple(c) for c in p["chunks"]]
         p["decodes"] = [tuple(d) for d in p["decodes"]]
         out.append({k: p[k] for k in ("iteration", "generated", "copies", "slots", "chunks",
-                                      "decodes", "admitted", "preempted", "finished")})
+                                      "decodes", "admitted", "preempted", "finished",
+                                      "swap_out", "swap_in")})
     assert s.num_free() == cfg["num_blocks"]
     s.close()
     return out
@@ -84,6 +86,32 @@ def test_plans_match_the_oracle(case, policy):
         assert g == w, f"iteration {w['iteration']} differs"
 
 
+SWAP_CASES = {
+    "tight_pool": CASES["tight_pool"],
+    "tiny_blocks_tight": (dict(num_blocks=44, block_size=2, max_seqs=6, max_tokens=24,
+                               max_chunk=5, max_len=40),
+                          dict(n=40, prompt=(1, 20), output=(1, 20), multi_frac=0.4,
+                               samples=2, arrival_every=1)),
+}
+
+
+@pytest.mark.parametrize("host_blocks", [4, 24, 200])
+@pytest.mark.parametrize("case", sorted(SWAP_CASES))
+def test_swapping_plans_match_the_oracle(case, host_blocks):
+    cfg, stream = SWAP_CASES[case]
+    cfg = dict(cfg, num_host_blocks=host_blocks)
+    reqs = make_request_stream(12, **stream)
+    order = np.random.default_rng(len(case) + host_blocks).permutation(cfg["num_blocks"])
+    want = oracle_packets(cfg, "paged", order, reqs)
+    got = native_packets(cfg, "paged", order, reqs)
+    assert len(got) == len(want)
+    for w, g in zip(want, got):
+        assert g == w, f"iteration {w['iteration']} differs"
+    assert sum(len(p["preempted"]) for p in want) > 0
+    if host_blocks >= 24:   # with 4 host blocks most victims fall back to recomputation
+        assert sum(len(p["swap_out"]) for p in want) > 0
+
+
 def test_long_tail_stream_matches_the_oracle():
     cfg = dict(num_blocks=400, block_size=16, max_seqs=64, max_tokens=512, max_chunk=256,
                max_len=1600)
@@ -109,6 +137,9 @@ def test_create_rejects_bad_arguments():
     bad = dict(cfg, max_chunk=0)
     with pytest.raises(PAError):
         Scheduler(policy="paged", free_order=range(4), requests=[(4, [1], 0)], **bad)
+    with pytest.raises(PAError):   # host blocks serve the paged policy only
+        Scheduler(policy="reserve", free_order=range(4), requests=[(4, [1], 0)],
+                  num_host_blocks=4, **cfg)
 
 
 def test_empty_stream_is_finished_at_once():
