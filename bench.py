@@ -416,7 +416,10 @@ ENGINE_DESC = ("iteration-level serving loop (no model weights): 1024 requests a
                "head_dim 128, block_size 16, bf16; pool 8192 blocks (512 MB); at most 256 "
                "running samples, 2048 tokens and 512-token prefill chunks per iteration, "
                "max_len 2048 (reservation: 128 blocks per sample); the paged policy also on "
-               "a 3072-block pool, evicting by recomputation or by swapping to pinned host memory")
+               "a 3072-block pool, evicting by recomputation or by swapping to pinned host memory; "
+               "and a second stream whose requests name one of 16 shared 512-token prompt "
+               "prefixes (suffixes U[32, 256], outputs clipped at 1280), with and without prefix "
+               "caching")
 
 
 def engine_rows(pa, torch, oracle_on: bool) -> dict:
@@ -446,10 +449,15 @@ def engine_rows(pa, torch, oracle_on: bool) -> dict:
     qd = torch.randn(S, HQ, D, generator=g, device="cuda").bfloat16()
     outp, outd = torch.empty_like(qp), torch.empty_like(qd)
     scale = 1.0 / np.sqrt(D)
-    want = sum(sum(o) for _, o, _ in reqs)
 
-    def run(policy, stream_reqs, num_blocks=None, host_blocks=0):
-        c = dict(cfg, num_blocks=num_blocks or cfg["num_blocks"], num_host_blocks=host_blocks)
+    # a second stream for prefix caching: 16 shared 512-token prompt prefixes
+    preqs = make_request_stream(283, 1024, prompt=(32, 256), multi_frac=0.2, samples=4,
+                                output_lognormal=(128, 1.0, 1280), prefix_groups=16,
+                                prefix_tokens=512)
+
+    def run(policy, stream_reqs, num_blocks=None, host_blocks=0, prefix=False):
+        c = dict(cfg, num_blocks=num_blocks or cfg["num_blocks"], num_host_blocks=host_blocks,
+                 prefix_caching=prefix)
         ws = pa.new_decode_workspace(S, HQ, D, cfg["max_len"])
         sched = runtime.Scheduler(policy=policy, requests=stream_reqs, **c,
                                   free_order=order if num_blocks is None
@@ -466,15 +474,21 @@ def engine_rows(pa, torch, oracle_on: bool) -> dict:
         return st, wall
 
     run("paged", reqs[:64])   # first launches of every kernel, outside the timed runs
-    out = {"workload": ENGINE_DESC, "output_tokens": want, "policies": {}}
+    out = {"workload": ENGINE_DESC, "output_tokens": sum(sum(x[1]) for x in reqs),
+           "prefix_stream_output_tokens": sum(sum(x[1]) for x in preqs), "policies": {}}
     # the paged policy again on a pool of 3072 blocks (192 MB), where it must
     # evict: dropping and recomputing victims, or swapping them to 4096
     # pinned host blocks (256 MB)
-    runs = [("paged", "paged", None, 0), ("reserve", "reserve", None, 0),
-            ("static", "static", None, 0), ("paged_3072_recompute", "paged", 3072, 0),
-            ("paged_3072_swap", "paged", 3072, 4096)]
-    for name, policy, nblk, hblk in runs:
-        st, wall = run(policy, reqs, nblk, hblk)
+    # and the paged policy on the prefix stream, without and with prefix caching
+    runs = [("paged", "paged", reqs, None, 0, False), ("reserve", "reserve", reqs, None, 0, False),
+            ("static", "static", reqs, None, 0, False),
+            ("paged_3072_recompute", "paged", reqs, 3072, 0, False),
+            ("paged_3072_swap", "paged", reqs, 3072, 4096, False),
+            ("prefix_stream_paged", "paged", preqs, None, 0, False),
+            ("prefix_stream_paged_cached", "paged", preqs, None, 0, True)]
+    for name, policy, rq, nblk, hblk, prefix in runs:
+        st, wall = run(policy, rq, nblk, hblk, prefix)
+        want = sum(sum(x[1]) for x in rq)
         kv = st["decode_context_tokens"] * 2 * HKV * D * 2
         it = st["iterations"]
         out["policies"][name] = {

@@ -66,6 +66,7 @@ typedef struct {
   int32_t policy;     /* PA_POLICY_* */
   int32_t num_host_blocks; /* PAGED only: host blocks for swapping evicted requests
                               (0: an evicted request is dropped and recomputed) */
+  int32_t prefix_caching;  /* PAGED only, nonzero: reuse full prefix blocks across requests */
 } pa_sched_config;
 
 typedef struct pa_sched pa_sched;
@@ -82,13 +83,19 @@ typedef struct pa_sched pa_sched;
  *                   sample_offsets[r] .. sample_offsets[r+1]-1 (at least one)
  *   output_lens     [sample_offsets[num_requests]] tokens each sample
  *                   generates, >= 1 (the first comes from the prompt's prefill)
+ *   prefix_ids      [num_requests] or NULL: the shared prompt prefix a request
+ *                   names (-1: none); requests naming one id share its first
+ *                   prefix_lens[r] prompt tokens ("Module 4", section "Block
+ *                   sharing", on sharing identical prefixes across requests)
+ *   prefix_lens     [num_requests] or NULL: 0 <= prefix_lens[r] <= prompt_lens[r]
  * Returns PA_OK and *out, or PA_ERR_NULL / PA_ERR_SHAPE (bad config, bad
  * free_order, or a request that exceeds max_len, max_seqs or the pool even
  * when alone).
  */
 int pa_sched_create(const pa_sched_config* cfg, const int32_t* free_order, int32_t num_requests,
                     const int32_t* prompt_lens, const int32_t* arrival,
-                    const int32_t* sample_offsets, const int32_t* output_lens, pa_sched** out);
+                    const int32_t* sample_offsets, const int32_t* output_lens,
+                    const int32_t* prefix_ids, const int32_t* prefix_lens, pa_sched** out);
 void pa_sched_destroy(pa_sched* s);
 
 /* Words (int32) a plan packet may take for this scheduler. */
@@ -136,6 +143,15 @@ int32_t pa_sched_num_free(const pa_sched* s);
  *      the prompt's blocks.
  *   7. Samples that produced their last token release their blocks and slot
  *      (STATIC: the whole batch releases when its last sample is done).
+ *
+ * Prefix caching (PAGED, prefix_caching nonzero): a full block inside a
+ * request's prefix, once prefilled, enters a cache under (prefix id, block
+ * index); the cache holds a reference to it. An admitted request takes the
+ * cached blocks of its prefix from block 0 up to the first miss (never its
+ * whole prompt) and prefills only the rest. Entries are kept in
+ * least-recently-used order (a hit or an entry moves to the back); when a
+ * block is needed and none is free, the oldest entry that only the cache
+ * holds gives its block up. Such blocks count as free in every fit test.
  *
  * The plan packet written to `buf` (int32 words):
  *   header [16]: 0 iteration, 1 tokens generated, 2 copies, 3 slots (tokens

@@ -58,7 +58,19 @@ the design notes):
     sharing kept, the host blocks released in the same order. A swapped-in
     request needs no prefill and takes no token budget; it decodes from the
     next iteration on. In one iteration the GPU runs the swap-outs, then the
-    swap-ins, then the copies, appends and attention.
+    swap-ins, then the copies, appends and attention;
+  * prefix caching (paged, when enabled; "Module 4", section "Block sharing",
+    its note on sharing identical prefixes across requests): a request may
+    name a prefix -- (prefix id, length): its first `length` prompt tokens
+    equal those of every request naming the same id. A full block inside the
+    prefix, once prefilled, is entered in a cache under (prefix id, block
+    index), and the cache holds a reference to it. An admitted request takes
+    the cached blocks of its prefix from block 0 up to the first miss (never
+    its whole prompt: the last prompt token is always computed) and starts
+    its prefill after them. Cache entries are kept in least-recently-used
+    order (a hit or an entry moves a key to the back); when a block is needed
+    and none is free, the oldest entry that only the cache still holds gives
+    up its block. Those blocks count as free in every fit test.
 """
 from __future__ import annotations
 
@@ -78,6 +90,7 @@ class SchedConfig:
     max_len: int       # longest context a sample may reach (prompt + output - 1)
     policy: str = "paged"
     num_host_blocks: int = 0   # paged: host blocks for swapping (0: evictions recompute)
+    prefix_caching: bool = False   # paged: reuse full prefix blocks across requests
 
 
 @dataclass
@@ -108,11 +121,13 @@ class _Sample:
 
 
 class _Request:
-    def __init__(self, rid, prompt, outs, arrival):
+    def __init__(self, rid, prompt, outs, arrival, prefix_id=-1, prefix_len=0):
         self.rid = rid
         self.prompt = int(prompt)
         self.outs = [int(o) for o in outs]
         self.arrival = int(arrival)
+        self.prefix_id = int(prefix_id)
+        self.prefix_len = int(prefix_len) if prefix_id >= 0 else 0
         self.reset()
         self.evictions = 0
 
@@ -135,7 +150,8 @@ def _cdiv(a, b):
 class Scheduler:
     """Drives requests through prefill and decode, one ``step()`` per iteration.
 
-    ``requests`` is a list of (prompt_len, [output_len per sample], arrival_iteration),
+    ``requests`` is a list of (prompt_len, [output_len per sample], arrival_iteration)
+    or (prompt_len, [output_len per sample], arrival_iteration, prefix_id, prefix_len),
     in arrival order; ``free_order`` lists every block id once.
     """
 
@@ -144,6 +160,8 @@ class Scheduler:
             raise ValueError(f"unknown policy {cfg.policy!r}")
         if cfg.num_host_blocks < 0 or (cfg.num_host_blocks > 0 and cfg.policy != "paged"):
             raise ValueError("host blocks serve the paged policy's evictions only")
+        if cfg.prefix_caching and cfg.policy != "paged":
+            raise ValueError("prefix caching needs the paged policy")
         self.cfg = cfg
         order = [int(b) for b in free_order]
         if sorted(order) != list(range(cfg.num_blocks)):
@@ -151,11 +169,15 @@ class Scheduler:
         self.free = order[::-1]               # a stack: free[-1] is taken next
         self.ref = [0] * cfg.num_blocks
         self.host_free = list(range(cfg.num_host_blocks))[::-1]   # host block 0 first
+        self.cache = {}    # (prefix id, block index) -> block
+        self.lru = []      # cache keys, least recently used first
         self.reqs = []
-        for i, (p, outs, arr) in enumerate(requests):
-            r = _Request(i, p, outs, arr)
+        for i, req in enumerate(requests):
+            r = _Request(i, *req)
             if r.prompt < 1 or r.n < 1 or min(r.outs) < 1:
                 raise ValueError(f"request {i}: empty prompt or output")
+            if not 0 <= r.prefix_len <= r.prompt:
+                raise ValueError(f"request {i}: prefix longer than the prompt")
             if r.prompt + max(r.outs) - 1 > cfg.max_len:
                 raise ValueError(f"request {i} exceeds max_len")
             worst = r.n * _cdiv(cfg.max_len if cfg.policy != "paged"
@@ -172,10 +194,35 @@ class Scheduler:
 
     # -- block manager ---------------------------------------------------------------
     def _alloc(self):
+        if not self.free:   # the oldest cache entry nobody else holds gives up its block
+            key = next(k for k in self.lru if self.ref[self.cache[k]] == 1)
+            self.lru.remove(key)
+            b = self.cache.pop(key)
+            self.ref[b] = 0
+            self.free.append(b)
         b = self.free.pop()
         assert self.ref[b] == 0
         self.ref[b] = 1
         return b
+
+    def _available(self):
+        """Blocks an allocation can get: free ones and cached ones only the cache holds."""
+        return len(self.free) + sum(1 for b in self.cache.values() if self.ref[b] == 1)
+
+    def _prefix_hits(self, r):
+        """Cached blocks of r's prefix from block 0 up to the first miss."""
+        if not self.cfg.prefix_caching or r.prefix_id < 0:
+            return []
+        bs, hits = self.cfg.block_size, []
+        limit = min(r.prefix_len, r.prompt - 1)
+        while (len(hits) + 1) * bs <= limit and (r.prefix_id, len(hits)) in self.cache:
+            hits.append(self.cache[(r.prefix_id, len(hits))])
+        return hits
+
+    def _touch(self, key):
+        if key in self.lru:
+            self.lru.remove(key)
+        self.lru.append(key)
 
     def _release_table(self, table):
         for b in table:
@@ -227,7 +274,7 @@ class Scheduler:
             for h in q.host_table:
                 if h not in uniq:
                     uniq.append(h)
-        if self.slots_used + len(live) > self.cfg.max_seqs or len(uniq) > len(self.free):
+        if self.slots_used + len(live) > self.cfg.max_seqs or len(uniq) > self._available():
             return False
         where = {}
         for h in uniq:
@@ -305,7 +352,16 @@ class Scheduler:
         q_start = len(pre_slots)
         for pos in range(r.prefilled, r.prefilled + L):
             pre_slots.append(self._write_slot(r.table, pos, plan.copies))
+        before = r.prefilled
         r.prefilled += L
+        if cfg.prefix_caching and r.prefix_id >= 0:   # full prefix blocks this chunk completed
+            bs = cfg.block_size
+            for j in range(before // bs, r.prefilled // bs):
+                key = (r.prefix_id, j)
+                if (j + 1) * bs <= r.prefix_len and key not in self.cache:
+                    self.cache[key] = r.table[j]
+                    self.ref[r.table[j]] += 1
+                    self._touch(key)
         plan.chunks.append((rid, q_start, L, r.prefilled, list(r.table)))
         if r.prefilled == r.prompt:          # the prompt's last chunk: fork into samples
             r.state = "decode"
@@ -342,7 +398,7 @@ class Scheduler:
         budget = cfg.max_tokens
         # eviction until the running requests' appends of this iteration fit
         if cfg.policy == "paged":
-            while self._need(budget) > len(self.free):
+            while self._need(budget) > self._available():
                 if len(self.running) <= 1:
                     raise AssertionError("a lone request does not fit the pool")
                 self._evict(self.running[-1], plan)
@@ -376,9 +432,14 @@ class Scheduler:
                 continue
             if self.slots_used + r.n > cfg.max_seqs:
                 break
+            hits = []
             if cfg.policy == "paged":
-                first = min(r.prompt, cfg.max_chunk, budget)
-                if _cdiv(first, cfg.block_size) > len(self.free):
+                hits = self._prefix_hits(r)
+                got = len(hits) * cfg.block_size
+                first = min(r.prompt - got, cfg.max_chunk, budget)
+                held_by_cache_only = sum(1 for b in hits if self.ref[b] == 1)
+                if _cdiv(got + first, cfg.block_size) - len(hits) > \
+                        self._available() - held_by_cache_only:
                     break
             else:
                 R = _cdiv(cfg.max_len, cfg.block_size)
@@ -391,6 +452,11 @@ class Scheduler:
             self.slots_used += r.n
             r.state = "prefill"
             plan.admitted.append(rid)
+            for j, b in enumerate(hits):   # the cached prefix blocks: no prefill
+                self.ref[b] += 1
+                r.table.append(b)
+                self._touch((r.prefix_id, j))
+            r.prefilled = len(hits) * cfg.block_size
             budget -= self._chunk(rid, plan, budget, pre_slots)
         plan.slots = pre_slots + dec_slots
         # release what finished in this iteration (after its kernels have run)

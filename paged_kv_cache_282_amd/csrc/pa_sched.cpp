@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <chrono>
 #include <deque>
+#include <map>
 #include <vector>
 
 #include "pa.h"
@@ -35,6 +36,7 @@ class BlockPool {
   }
   void share(int32_t b) { ++refs_[b]; }
   bool shared(int32_t b) const { return refs_[b] > 1; }
+  int32_t users(int32_t b) const { return refs_[b]; }
   void drop(int32_t b) {
     if (--refs_[b] == 0) free_.push_back(b);
   }
@@ -60,6 +62,7 @@ enum class Phase { kQueued, kPrefill, kDecode, kSwapped, kDone };
 
 struct Req {
   int32_t prompt = 0, arrival = 0;
+  int32_t prefix_id = -1, prefix_len = 0;  // shared prompt prefix (id -1: none)
   std::vector<int32_t> outs;
   Phase phase = Phase::kQueued;
   int32_t prefilled = 0;
@@ -106,8 +109,55 @@ struct pa_sched {
   int32_t slots_used = 0;
   std::vector<int32_t> owed_copies;
   std::vector<int32_t> host_free;  // stack of host blocks for swapped requests
+  // Prefix cache: (prefix id, block index) -> block, holding one reference
+  // to it; keys in least-recently-used order.
+  std::map<int64_t, int32_t> cache;
+  std::vector<int64_t> lru;
   int32_t iteration = 0;
   PlanBuf plan;
+
+  static int64_t prefix_key(int32_t id, int32_t j) {
+    return (static_cast<int64_t>(id) << 32) | static_cast<uint32_t>(j);
+  }
+  void touch(int64_t key) {
+    auto it = std::find(lru.begin(), lru.end(), key);
+    if (it != lru.end()) lru.erase(it);
+    lru.push_back(key);
+  }
+  // A block: the free stack's top, or, with none free, the block of the
+  // oldest cache entry that only the cache still holds.
+  int32_t alloc() {
+    if (pool.free_count() == 0) {
+      for (auto it = lru.begin(); it != lru.end(); ++it) {
+        const int32_t b = cache.at(*it);
+        if (pool.users(b) == 1) {
+          cache.erase(*it);
+          lru.erase(it);
+          pool.drop(b);
+          break;
+        }
+      }
+    }
+    return pool.take();
+  }
+  // Blocks an allocation can get: free ones and cached ones only the cache holds.
+  int64_t available() const {
+    int64_t n = pool.free_count();
+    for (const auto& kv : cache) n += pool.users(kv.second) == 1 ? 1 : 0;
+    return n;
+  }
+  // Cached blocks of r's prefix from block 0 up to the first miss.
+  std::vector<int32_t> prefix_hits(const Req& r) const {
+    std::vector<int32_t> hits;
+    if (!cfg.prefix_caching || r.prefix_id < 0) return hits;
+    const int32_t limit = std::min(r.prefix_len, r.prompt - 1);
+    for (int32_t j = 0; (j + 1) * cfg.block_size <= limit; ++j) {
+      auto it = cache.find(prefix_key(r.prefix_id, j));
+      if (it == cache.end()) break;
+      hits.push_back(it->second);
+    }
+    return hits;
+  }
 
   bool finished() const {
     return next_arrival == reqs.size() && queue.empty() && running.empty();
@@ -118,9 +168,9 @@ struct pa_sched {
   int32_t slot_for(std::vector<int32_t>& table, int32_t pos) {
     const int32_t j = pos / cfg.block_size;
     if (j == static_cast<int32_t>(table.size())) {
-      table.push_back(pool.take());
+      table.push_back(alloc());
     } else if (pool.shared(table[j])) {
-      const int32_t fresh = pool.take();
+      const int32_t fresh = alloc();
       plan.copies.push_back(table[j]);
       plan.copies.push_back(fresh);
       pool.drop(table[j]);
@@ -206,12 +256,11 @@ struct pa_sched {
     int32_t live = 0;
     for (const Seq& q : r.seqs) live += q.released ? 0 : 1;
     const std::vector<int32_t> host = distinct(r, [](const Seq& q) { return q.host_table; });
-    if (slots_used + live > cfg.max_seqs ||
-        static_cast<int64_t>(host.size()) > pool.free_count())
+    if (slots_used + live > cfg.max_seqs || static_cast<int64_t>(host.size()) > available())
       return false;
     std::vector<int32_t> dev(host.size());
     for (size_t i = 0; i < host.size(); ++i) {
-      dev[i] = pool.take();
+      dev[i] = alloc();
       plan.swap_in.push_back(host[i]);
       plan.swap_in.push_back(dev[i]);
     }
@@ -275,7 +324,18 @@ struct pa_sched {
     plan.chunk_start.push_back(static_cast<int32_t>(plan.pre_slots.size()));
     for (int32_t pos = r.prefilled; pos < r.prefilled + L; ++pos)
       plan.pre_slots.push_back(slot_for(r.prompt_table, pos));
+    const int32_t before = r.prefilled;
     r.prefilled += L;
+    if (cfg.prefix_caching && r.prefix_id >= 0) {  // full prefix blocks this chunk completed
+      for (int32_t j = before / cfg.block_size; j < r.prefilled / cfg.block_size; ++j) {
+        const int64_t key = prefix_key(r.prefix_id, j);
+        if ((j + 1) * cfg.block_size <= r.prefix_len && !cache.count(key)) {
+          cache[key] = r.prompt_table[j];
+          pool.share(r.prompt_table[j]);
+          touch(key);
+        }
+      }
+    }
     plan.chunk_ctx.push_back(r.prefilled);
     put_table(plan.chunk_tab, r.prompt_table);
     plan.longest_chunk = std::max(plan.longest_chunk, L);
@@ -315,23 +375,35 @@ struct pa_sched {
     const int32_t rid = queue.front();
     Req& r = reqs[rid];
     if (slots_used + r.width() > cfg.max_seqs) return false;
+    std::vector<int32_t> hits;
     if (cfg.policy == PA_POLICY_PAGED) {
-      if (cdiv(std::min(std::min(r.prompt, cfg.max_chunk), budget), cfg.block_size) >
-          pool.free_count())
+      hits = prefix_hits(r);
+      const int32_t got = static_cast<int32_t>(hits.size()) * cfg.block_size;
+      const int32_t first = std::min(std::min(r.prompt - got, cfg.max_chunk), budget);
+      int64_t held_by_cache_only = 0;
+      for (int32_t b : hits) held_by_cache_only += pool.users(b) == 1 ? 1 : 0;
+      if (cdiv(got + first, cfg.block_size) - static_cast<int64_t>(hits.size()) >
+          available() - held_by_cache_only)
         return false;
     } else {
       const int32_t per = cdiv(cfg.max_len, cfg.block_size);
       if (static_cast<int64_t>(per) * r.width() > pool.free_count()) return false;
-      for (int32_t i = 0; i < per; ++i) r.prompt_table.push_back(pool.take());
+      for (int32_t i = 0; i < per; ++i) r.prompt_table.push_back(alloc());
       r.spare.assign(r.outs.size() - 1, {});
       for (auto& t : r.spare)
-        for (int32_t i = 0; i < per; ++i) t.push_back(pool.take());
+        for (int32_t i = 0; i < per; ++i) t.push_back(alloc());
     }
     queue.pop_front();
     running.push_back(rid);
     slots_used += r.width();
     r.phase = Phase::kPrefill;
     plan.admitted.push_back(rid);
+    for (size_t j = 0; j < hits.size(); ++j) {  // the cached prefix blocks: no prefill
+      pool.share(hits[j]);
+      r.prompt_table.push_back(hits[j]);
+      touch(prefix_key(r.prefix_id, static_cast<int32_t>(j)));
+    }
+    r.prefilled = static_cast<int32_t>(hits.size()) * cfg.block_size;
     return true;
   }
 
@@ -387,7 +459,7 @@ struct pa_sched {
     const bool batch_open = running.empty();
     int32_t budget = cfg.max_tokens;
     if (cfg.policy == PA_POLICY_PAGED) {
-      while (blocks_wanted(budget) > pool.free_count()) {
+      while (blocks_wanted(budget) > available()) {
         if (running.size() <= 1) return PA_ERR_STATE;
         evict(running.back());
       }
@@ -624,7 +696,8 @@ extern "C" {
 
 int pa_sched_create(const pa_sched_config* cfg, const int32_t* free_order, int32_t num_requests,
                     const int32_t* prompt_lens, const int32_t* arrival,
-                    const int32_t* sample_offsets, const int32_t* output_lens, pa_sched** out) {
+                    const int32_t* sample_offsets, const int32_t* output_lens,
+                    const int32_t* prefix_ids, const int32_t* prefix_lens, pa_sched** out) {
   if (!cfg || !out || !free_order || (num_requests > 0 && (!prompt_lens || !arrival ||
                                                            !sample_offsets || !output_lens)))
     return PA_ERR_NULL;
@@ -633,7 +706,8 @@ int pa_sched_create(const pa_sched_config* cfg, const int32_t* free_order, int32
   if (c.num_blocks <= 0 || c.block_size <= 0 || c.max_seqs <= 0 || c.max_tokens <= 0 ||
       c.max_chunk <= 0 || c.max_len <= 0 || num_requests < 0 || c.policy < PA_POLICY_PAGED ||
       c.policy > PA_POLICY_STATIC || c.num_host_blocks < 0 ||
-      (c.num_host_blocks > 0 && c.policy != PA_POLICY_PAGED))
+      (c.num_host_blocks > 0 && c.policy != PA_POLICY_PAGED) ||
+      (c.prefix_caching != 0 && c.policy != PA_POLICY_PAGED))
     return PA_ERR_SHAPE;
   std::vector<char> seen(c.num_blocks, 0);
   for (int32_t i = 0; i < c.num_blocks; ++i) {
@@ -651,8 +725,13 @@ int pa_sched_create(const pa_sched_config* cfg, const int32_t* free_order, int32
     Req& q = s->reqs[r];
     q.prompt = prompt_lens[r];
     q.arrival = arrival[r];
+    if (prefix_ids && prefix_ids[r] >= 0) {
+      q.prefix_id = prefix_ids[r];
+      q.prefix_len = prefix_lens ? prefix_lens[r] : 0;
+    }
     const int32_t a = sample_offsets[r], b = sample_offsets[r + 1];
-    bool ok = q.prompt >= 1 && b > a && (r == 0 || arrival[r] >= arrival[r - 1]);
+    bool ok = q.prompt >= 1 && b > a && (r == 0 || arrival[r] >= arrival[r - 1]) &&
+              q.prefix_len >= 0 && q.prefix_len <= q.prompt;
     int32_t longest = 0;
     for (int32_t k = a; ok && k < b; ++k) {
       ok = output_lens[k] >= 1;

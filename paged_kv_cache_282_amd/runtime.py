@@ -23,7 +23,8 @@ _i64 = ctypes.c_int64
 
 class _Config(ctypes.Structure):
     _fields_ = [("num_blocks", _i), ("block_size", _i), ("max_seqs", _i), ("max_tokens", _i),
-                ("max_chunk", _i), ("max_len", _i), ("policy", _i), ("num_host_blocks", _i)]
+                ("max_chunk", _i), ("max_len", _i), ("policy", _i), ("num_host_blocks", _i),
+                ("prefix_caching", _i)]
 
 
 class EngineStats(ctypes.Structure):
@@ -39,7 +40,7 @@ class EngineStats(ctypes.Structure):
 def _lib():
     lib = load()
     if not getattr(lib, "_sched_ready", False):
-        lib.pa_sched_create.argtypes = [ctypes.POINTER(_Config), _p, _i, _p, _p, _p, _p,
+        lib.pa_sched_create.argtypes = [ctypes.POINTER(_Config), _p, _i, _p, _p, _p, _p, _p, _p,
                                         ctypes.POINTER(_p)]
         lib.pa_sched_create.restype = ctypes.c_int
         lib.pa_sched_destroy.argtypes = [_p]
@@ -100,24 +101,28 @@ def parse_plan(buf: np.ndarray) -> dict:
 
 
 class Scheduler:
-    """The C++ scheduler. ``requests``: (prompt_len, [output_len per sample], arrival)."""
+    """The C++ scheduler. ``requests``: (prompt_len, [output_len per sample], arrival)
+    or (prompt_len, [output_len per sample], arrival, prefix_id, prefix_len)."""
 
     def __init__(self, num_blocks, block_size, max_seqs, max_tokens, max_chunk, max_len,
-                 policy, free_order, requests, num_host_blocks=0):
+                 policy, free_order, requests, num_host_blocks=0, prefix_caching=False):
         self._lib = _lib()
         cfg = _Config(num_blocks, block_size, max_seqs, max_tokens, max_chunk, max_len,
-                      POLICIES[policy], num_host_blocks)
+                      POLICIES[policy], num_host_blocks, int(bool(prefix_caching)))
         prompts = _arr([r[0] for r in requests])
         arrival = _arr([r[2] for r in requests])
         offs = _arr(np.concatenate([[0], np.cumsum([len(r[1]) for r in requests])]))
         outs = _arr([o for r in requests for o in r[1]] or [0])
+        pids = _arr([r[3] if len(r) > 3 else -1 for r in requests] or [0])
+        plens = _arr([r[4] if len(r) > 4 else 0 for r in requests] or [0])
         order = _arr(free_order)
         if order.shape[0] != num_blocks:
             raise ValueError("free_order must list num_blocks ids")
         handle = _p()
         st = self._lib.pa_sched_create(ctypes.byref(cfg), order.ctypes.data, len(requests),
                                        prompts.ctypes.data, arrival.ctypes.data,
-                                       offs.ctypes.data, outs.ctypes.data, ctypes.byref(handle))
+                                       offs.ctypes.data, outs.ctypes.data, pids.ctypes.data,
+                                       plens.ctypes.data, ctypes.byref(handle))
         if st != 0:
             raise PAError("pa_sched_create", st)
         self.handle = handle

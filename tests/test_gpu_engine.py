@@ -39,18 +39,22 @@ def _nan_pool(nb, dtype):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("policy,dtype,host_blocks", [("paged", "bf16", 0), ("paged", "f32", 0),
-                                                      ("paged", "bf16", 24),
-                                                      ("reserve", "bf16", 0),
-                                                      ("static", "f32", 0)])
-def test_engine_matches_the_oracle_every_iteration(policy, dtype, host_blocks):
-    print(f"\nengine parity: policy={policy} dtype={dtype} host blocks={host_blocks}",
-          flush=True)
+@pytest.mark.parametrize("policy,dtype,host_blocks,prefix", [
+    ("paged", "bf16", 0, False), ("paged", "f32", 0, False), ("paged", "bf16", 24, False),
+    ("paged", "bf16", 0, True), ("reserve", "bf16", 0, False), ("static", "f32", 0, False)])
+def test_engine_matches_the_oracle_every_iteration(policy, dtype, host_blocks, prefix):
+    print(f"\nengine parity: policy={policy} dtype={dtype} host blocks={host_blocks} "
+          f"prefix caching={prefix}", flush=True)
     # 20 blocks of 16 tokens: tight enough that the paged policy evicts
     cfg = dict(num_blocks=20, block_size=BS, max_seqs=6, max_tokens=48, max_chunk=32,
-               max_len=128, num_host_blocks=host_blocks)
-    reqs = make_request_stream(21, 14, prompt=(1, 70), output=(1, 40), multi_frac=0.3,
-                               samples=2, arrival_every=2)
+               max_len=128, num_host_blocks=host_blocks, prefix_caching=prefix)
+    if prefix:   # two shared 40-token prompt prefixes
+        reqs = make_request_stream(21, 14, prompt=(1, 30), output=(1, 40), multi_frac=0.3,
+                                   samples=2, arrival_every=2, prefix_groups=2,
+                                   prefix_tokens=40)
+    else:
+        reqs = make_request_stream(21, 14, prompt=(1, 70), output=(1, 40), multi_frac=0.3,
+                                   samples=2, arrival_every=2)
     order = np.random.default_rng(2).permutation(cfg["num_blocks"])
     mb = -(-cfg["max_len"] // BS)
     scale = 1.0 / np.sqrt(D)
@@ -120,8 +124,8 @@ def test_engine_matches_the_oracle_every_iteration(policy, dtype, host_blocks):
         n_copies += len(want.copies)
         n_evict += len(want.preempted)
     eng.close()
-    assert sched.num_free() == cfg["num_blocks"]
-    assert n_dec > 0 and n_pre > 0 and n_copies > 0
+    assert sched.num_free() + len(osched.cache) == cfg["num_blocks"]
+    assert n_dec > 0 and n_pre > 0 and (n_copies > 0 or prefix)
     assert n_evict > 0 or policy != "paged"
     assert n_swap > 0 or host_blocks == 0
     print(f"  {osched.it} iterations, {n_pre} prefill tokens, {n_dec} decodes, "

@@ -52,6 +52,14 @@ SCHED_MUTATIONS = {
     "prefill_token_not_counted": ("self.gen = 1 ", "self.gen = 0 "),
     "swap_in_forgets_sharing": ("self.ref[b] = sum(q.table.count(b) for q in live)", "pass"),
     "swap_out_skips_host_order": ("where[b] = self.host_free.pop()", "where[b] = self.host_free.pop(0)"),
+    "cache_evicts_newest": ("key = next(k for k in self.lru if", "key = next(k for k in self.lru[::-1] if"),
+    "cache_hit_past_a_miss": (
+        "        while (len(hits) + 1) * bs <= limit and (r.prefix_id, len(hits)) in self.cache:\n"
+        "            hits.append(self.cache[(r.prefix_id, len(hits))])\n",
+        "        hits = [self.cache[(r.prefix_id, j)] for j in range(limit // bs)\n"
+        "                if (r.prefix_id, j) in self.cache]\n"),
+    "cache_takes_partial_block": ("if (j + 1) * bs <= r.prefix_len and key not in self.cache:",
+                                  "if j * bs < r.prefix_len and key not in self.cache:"),
 }
 
 

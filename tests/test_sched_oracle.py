@@ -131,7 +131,7 @@ def _check_invariants(s, plans, reqs, bs):
     fin = [r for p in plans for r in p.finished]
     assert sorted(fin) == list(range(len(reqs)))
     made = sum(p.generated for p in plans)
-    want = sum(sum(o) for _, o, _ in reqs)
+    want = sum(sum(r[1]) for r in reqs)
     evictions = sum(len(p.preempted) for p in plans)
     if s.cfg.policy != "paged":
         assert evictions == 0 and made == want
@@ -286,3 +286,63 @@ def test_swapping_keeps_progress_and_returns_every_block(seed):
     assert not held
     _check_invariants(s, plans, reqs, 8)
     assert sorted(s.host_free) == list(range(64))
+
+
+def test_hand_derived_prefix_cache_trace():
+    # bs 4, blocks 0..9 handed out in order. A and B name prefix 0 of 9
+    # tokens (two full blocks); prompts of 12, two tokens each; B arrives at
+    # iteration 1. A's prefill enters blocks 0 and 1 in the cache (block 2
+    # holds token 8, past the last full prefix block). B takes them as hits
+    # and prefills only positions 8..11, into block 4 (3 went to A's decode).
+    cfg = SchedConfig(num_blocks=10, block_size=4, max_seqs=4, max_tokens=16, max_chunk=16,
+                      max_len=16, policy="paged", prefix_caching=True)
+    s = Scheduler(cfg, list(range(10)), [(12, [2], 0, 0, 9), (12, [2], 1, 0, 9)])
+    p0, p1, p2 = s.step(), s.step(), s.step()
+    assert s.step() is None
+    assert p0.chunks == [(0, 0, 12, 12, [0, 1, 2])]
+    assert p1.chunks == [(1, 0, 4, 12, [0, 1, 4])]
+    assert p1.slots == [16, 17, 18, 19, 12]          # B's four tokens, then A's decode
+    assert p1.decodes == [(0, 0, 13, [0, 1, 2, 3])]
+    assert p2.decodes == [(1, 0, 13, [0, 1, 4, 3])]
+    # the cache keeps its blocks after both requests are done
+    assert s.cache == {(0, 0): 0, (0, 1): 1}
+    assert s.ref[0] == 1 and s.ref[1] == 1
+    assert sorted(s.free + [0, 1]) == list(range(10))
+
+
+def test_prefix_cache_gives_up_its_least_recently_used_block():
+    # bs 2, six blocks; four one-token-output requests with 4-token prefixes
+    # (two full blocks) and 5-token prompts, one per iteration, prefixes
+    # 0, 1, 2, 0. R2 needs a third block when none is free: the oldest entry,
+    # (0, 0) -> block 0, gives it up. R3's prefix then misses at block 0, so
+    # it takes no hit and prefills all five tokens, evicting (0, 1) -> 1 and
+    # (1, 0) -> 2 for its second and third blocks.
+    cfg = SchedConfig(num_blocks=6, block_size=2, max_seqs=2, max_tokens=8, max_chunk=8,
+                      max_len=6, policy="paged", prefix_caching=True)
+    reqs = [(5, [1], 0, 0, 4), (5, [1], 1, 1, 4), (5, [1], 2, 2, 4), (5, [1], 3, 0, 4)]
+    s = Scheduler(cfg, list(range(6)), reqs)
+    plans = _run(s, limit=20)
+    chunks = [c for p in plans for c in p.chunks]
+    assert chunks == [(0, 0, 5, 5, [0, 1, 2]), (1, 0, 5, 5, [2, 3, 4]),
+                      (2, 0, 5, 5, [4, 5, 0]), (3, 0, 5, 5, [0, 1, 2])]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_prefix_caching_saves_prefill_and_keeps_the_pool_whole(seed):
+    reqs = make_request_stream(seed, 60, prompt=(1, 40), output=(1, 40), multi_frac=0.2,
+                               samples=2, arrival_every=2, prefix_groups=3, prefix_tokens=50)
+    runs = {}
+    for pc in (False, True):
+        cfg = SchedConfig(num_blocks=80, block_size=8, max_seqs=10, max_tokens=64, max_chunk=32,
+                          max_len=140, policy="paged", prefix_caching=pc)
+        s = Scheduler(cfg, np.random.default_rng(seed).permutation(80), reqs)
+        plans = _run(s)
+        runs[pc] = sum(sum(c[2] for c in p.chunks) for p in plans)
+        fin = sorted(r for p in plans for r in p.finished)
+        assert fin == list(range(len(reqs)))
+        # every block is free or held by the cache alone
+        assert len(s.free) + len(s.cache) == 80
+        assert all(s.ref[b] == 1 for b in s.cache.values())
+        if not pc:
+            _check_invariants(s, plans, reqs, 8)
+    assert runs[True] < runs[False]

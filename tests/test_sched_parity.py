@@ -40,7 +40,7 @@ def oracle_packets(cfg: dict, policy, order, reqs):
     return out
 
 
-def native_packets(cfg: dict, policy, order, reqs):
+def native_packets(cfg: dict, policy, order, reqs, expect_free=True):
     s = Scheduler(policy=policy, free_order=order, requests=reqs, **cfg)
     out = []
     for p in s.run():
@@ -50,7 +50,8 @@ def native_packets(cfg: dict, policy, order, reqs):
         out.append({k: p[k] for k in ("iteration", "generated", "copies", "slots", "chunks",
                                       "decodes", "admitted", "preempted", "finished",
                                       "swap_out", "swap_in")})
-    assert s.num_free() == cfg["num_blocks"]
+    if expect_free:   # (a prefix cache keeps its blocks)
+        assert s.num_free() == cfg["num_blocks"]
     s.close()
     return out
 
@@ -110,6 +111,21 @@ def test_swapping_plans_match_the_oracle(case, host_blocks):
     assert sum(len(p["preempted"]) for p in want) > 0
     if host_blocks >= 24:   # with 4 host blocks most victims fall back to recomputation
         assert sum(len(p["swap_out"]) for p in want) > 0
+
+
+@pytest.mark.parametrize("host_blocks", [0, 24])
+@pytest.mark.parametrize("pool", [40, 80])
+def test_prefix_caching_plans_match_the_oracle(pool, host_blocks):
+    cfg = dict(num_blocks=pool, block_size=8, max_seqs=10, max_tokens=64, max_chunk=32,
+               max_len=140, prefix_caching=True, num_host_blocks=host_blocks)
+    reqs = make_request_stream(4, 60, prompt=(1, 40), output=(1, 40), multi_frac=0.2,
+                               samples=2, arrival_every=2, prefix_groups=3, prefix_tokens=50)
+    order = np.random.default_rng(pool).permutation(pool)
+    want = oracle_packets(cfg, "paged", order, reqs)
+    got = native_packets(cfg, "paged", order, reqs, expect_free=False)
+    assert len(got) == len(want)
+    for w, g in zip(want, got):
+        assert g == w, f"iteration {w['iteration']} differs"
 
 
 def test_long_tail_stream_matches_the_oracle():

@@ -14,7 +14,7 @@ import numpy as np
 
 def make_request_stream(seed: int, n: int, prompt=(1, 60), output=(1, 80),
                         multi_frac: float = 0.0, samples: int = 1, arrival_every: int = 0,
-                        output_lognormal=None):
+                        output_lognormal=None, prefix_groups: int = 0, prefix_tokens: int = 0):
     """``n`` requests as (prompt_len, [output_len per sample], arrival_iteration).
 
     prompt: inclusive uniform integer range. output: inclusive uniform range,
@@ -22,6 +22,11 @@ def make_request_stream(seed: int, n: int, prompt=(1, 60), output=(1, 80),
     clipped to [1, max]. A fraction ``multi_frac`` of the requests asks for
     ``samples`` samples, each with its own output length. Request i arrives at
     iteration ``i // arrival_every`` (all at 0 when arrival_every is 0).
+
+    With ``prefix_groups`` > 0, request i also names prefix i % prefix_groups:
+    its prompt is that prefix's ``prefix_tokens`` tokens followed by its own
+    ``prompt``-range suffix, and the tuple grows to (prompt_len, outputs,
+    arrival, prefix_id, prefix_len).
     """
     rng = np.random.default_rng(np.random.SeedSequence([seed, 0x5EED]))
     prompts = rng.integers(prompt[0], prompt[1] + 1, n)
@@ -35,5 +40,9 @@ def make_request_stream(seed: int, n: int, prompt=(1, 60), output=(1, 80),
             med, sig, top = output_lognormal
             outs = np.clip(np.rint(np.exp(np.log(med) + sig * rng.standard_normal(k))), 1, top)
         arr = i // arrival_every if arrival_every else 0
-        reqs.append((int(prompts[i]), [int(o) for o in outs], int(arr)))
+        if prefix_groups > 0:
+            reqs.append((int(prefix_tokens + prompts[i]), [int(o) for o in outs], int(arr),
+                         i % prefix_groups, int(prefix_tokens)))
+        else:
+            reqs.append((int(prompts[i]), [int(o) for o in outs], int(arr)))
     return reqs
