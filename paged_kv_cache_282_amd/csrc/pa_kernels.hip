@@ -1105,7 +1105,9 @@ __device__ __forceinline__ bool chunk_geometry(const PrefillArgs& a, int c, int 
 template <int D>
 struct PrefillSmem {
   uint16_t k[2][(D / 8) * kStep * 8];        // [slice][token][8], tokens of one step
-  uint16_t v[2][(kStep / 4) * D * 4];        // [4-token slice][dim][4]
+  // [slice pair c][dim][8]: tokens 4c..4c+3 (set a) then 16+4c..16+4c+3
+  // (set b), which is one lane's whole p.V operand for that dim
+  uint16_t v[2][(kStep / 8) * D * 8];
 };
 
 // One workgroup tile: positions x*kWaves*pos_per_wave .. of chunk c, kv head g.
@@ -1132,7 +1134,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
   const uint16_t* pool = static_cast<const uint16_t*>(a.pool);
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   // the two LDS buffers, through pointers that alias nothing else
-  constexpr int kK = (D / 8) * kStep * 8, kV = (kStep / 4) * D * 4;
+  constexpr int kK = (D / 8) * kStep * 8, kV = (kStep / 8) * D * 8;
   uint16_t* __restrict__ lk = &smem.k[0][0];
   uint16_t* __restrict__ lv = &smem.v[0][0];
 
@@ -1195,8 +1197,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int pc = u * 256 + static_cast<int>(threadIdx.x);
-      uint16_t* dst = pc < kChunks / 2 ? &lk[buf * kK + pc * 8] : &lv[buf * kV + (pc - kChunks / 2) * 8];
-      *reinterpret_cast<u32x4*>(dst) = pre[u];
+      if (pc < kChunks / 2) {
+        *reinterpret_cast<u32x4*>(&lk[buf * kK + pc * 8]) = pre[u];
+      } else {  // 4 tokens of dims 2dp and 2dp+1 of 4-token slice sl, 8 bytes each
+        const int pv = pc - kChunks / 2;
+        const int sl = pv / (D / 2), dp = pv - sl * (D / 2);
+        uint16_t* row = &lv[buf * kV + ((sl & 3) * D + 2 * dp) * 8 + (sl >> 2) * 4];
+        *reinterpret_cast<u32x2*>(row) = u32x2{pre[u][0], pre[u][1]};
+        *reinterpret_cast<u32x2*>(row + 8) = u32x2{pre[u][2], pre[u][3]};
+      }
     }
   };
   // One step from LDS: the K operands feed the scores, then the V operands are
@@ -1212,11 +1221,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
     eng.scores(kA, kB, sa, sb);
     u32x4 vv[VT];
 #pragma unroll
-    for (int j = 0; j < VT; ++j) {
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(&lv[buf * kV + (kg * D + 16 * j + r) * 4]);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(&lv[buf * kV + ((4 + kg) * D + 16 * j + r) * 4]);
-      vv[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
+    for (int j = 0; j < VT; ++j)
+      vv[j] = *reinterpret_cast<const u32x4*>(&lv[buf * kV + (kg * D + 16 * j + r) * 8]);
     eng.finish(sa, sb, vv, t0, kend_wg, lane, a.sl2e);
   };
   // Iteration s: fetch step s+2 into `fetch_into` (free: its step s went to
