@@ -63,6 +63,16 @@ __device__ __forceinline__ f32x4 ld16f(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
 }
 
+// Buffer descriptor of `bytes` bytes from `base` (raw: no stride, byte
+// offsets; out-of-range reads return zero). 0x00020000 is the descriptor's
+// format word for untyped 32-bit data on this target.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
+                                           0x00020000);
+}
+// Cache-policy bits of a buffer load: nt (nontemporal, streaming).
+constexpr int kNontemporal = 2;
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
@@ -190,33 +200,38 @@ struct Bf16Engine {
     // A step that will not be computed (live == false) still issues its loads,
     // so that the number of loads in flight is the same on every path, but it
     // reads block 0 and every lane of an instruction reads the same 16 bytes.
-    // The block bases are wave-uniform (scalar registers); each load adds the
-    // lane's constant offset and a compile-time displacement.
+    // Each load is a buffer load through a descriptor of one kv head's K or V
+    // tile: the tile base is wave-uniform (scalar registers), each lane adds
+    // its constant offset and a compile-time displacement, and the hardware
+    // returns zero for anything outside the tile. The loads carry the
+    // nontemporal hint: K/V are read once, and streaming them past the caches
+    // this way sustains a higher HBM read rate on this chip than plain loads.
     const int r = lane & 15, kg = lane >> 4;
     if (!live) blkA = blkB = 0;
     blkA = __builtin_amdgcn_readfirstlane(blkA);
     blkB = __builtin_amdgcn_readfirstlane(blkB);
     const uint16_t* bA = pool + static_cast<int64_t>(blkA) * blk_elems;
     const uint16_t* bB = (BS == 16) ? pool + static_cast<int64_t>(blkB) * blk_elems : bA;
-    const uint16_t* kta = bA + kofs;                                 // set a, slice 0
-    const uint16_t* ktb = bB + kofs + (BS == 16 ? 0 : 16 * 8);       // set b, slice 0
-    const uint16_t* vta = bA + vofs;                                 // set a, 4-token slice 0
-    const uint16_t* vtb = bB + vofs + (BS == 16 ? 0 : 4 * D * 4);    // set b, 4-token slice 0
-    // lane's K element offset (slice kg, token r) and V offset (4-token slice
-    // kg, dim r)
-    const uint32_t ko = live ? static_cast<uint32_t>((kg * BS + r) * 8) : 0u;
-    const uint32_t vo = live ? static_cast<uint32_t>((kg * D + r) * 4) : 0u;
-    constexpr int ks = 4 * BS * 8;  // next 4 slices of K
-    constexpr int vs = 16 * 4;      // next 16 dims of V
+    constexpr int kTile = BS * D * 2;  // bytes of one kv head's K (or V) tile
+    const auto kra = tile_rsrc(bA + kofs, kTile), krb = tile_rsrc(bB + kofs, kTile);
+    const auto vra = tile_rsrc(bA + vofs, kTile), vrb = tile_rsrc(bB + vofs, kTile);
+    // lane's K byte offset (slice kg, token r) and V byte offset (4-token
+    // slice kg, dim r); set b of a 32-slot block starts at token 16
+    const int ko = live ? (kg * BS + r) * 16 : 0;
+    const int vo = live ? (kg * D + r) * 8 : 0;
+    constexpr int kb = BS == 16 ? 0 : 16 * 16;     // set b: tokens 16.. of the same K slice
+    constexpr int vb = BS == 16 ? 0 : 4 * D * 8;   // set b: 4-token slices 4..7
+    constexpr int ks = 4 * BS * 16;  // next 4 slices of K
+    constexpr int vs = 16 * 8;       // next 16 dims of V
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kv.kA[s] = ld16(kta + ko + ks * s);
-      kv.kB[s] = ld16(ktb + ko + ks * s);
+      kv.kA[s] = __builtin_amdgcn_raw_buffer_load_b128(kra, ko + ks * s, 0, kNontemporal);
+      kv.kB[s] = __builtin_amdgcn_raw_buffer_load_b128(krb, ko + kb + ks * s, 0, kNontemporal);
     }
 #pragma unroll
     for (int j = 0; j < VT; ++j) {
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vta + vo + vs * j);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vtb + vo + vs * j);
+      const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(vra, vo + vs * j, 0, kNontemporal);
+      const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(vrb, vo + vb + vs * j, 0, kNontemporal);
       kv.vv[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   }
