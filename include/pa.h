@@ -88,7 +88,7 @@ enum {
 /* Tokens per split-K partition of pa_decode. A sequence of n tokens is cut at
  * multiples of PA_DECODE_PARTITION; the cut never depends on the rest of the
  * batch, so a sequence's output does not depend on batch composition. */
-#define PA_DECODE_PARTITION 512
+#define PA_DECODE_PARTITION 1024
 
 /*
  * pa_append_kv — write each new token's K and V into its block slot.

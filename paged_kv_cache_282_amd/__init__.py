@@ -21,7 +21,7 @@ __all__ = ["PAError", "load", "lib_path", "pa_append_kv", "pa_copy_blocks", "pa_
            "pa_swap_blocks", "SWAP_OUT", "SWAP_IN",
            "pa_status_string", "new_decode_workspace", "DECODE_PARTITION"]
 
-DECODE_PARTITION = 512  # PA_DECODE_PARTITION in include/pa.h
+DECODE_PARTITION = 1024  # PA_DECODE_PARTITION in include/pa.h
 SWAP_OUT, SWAP_IN = 0, 1  # PA_SWAP_OUT, PA_SWAP_IN
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -11,7 +11,7 @@
 //     section "The prefill/decode mix": prefill chunks in the same iteration.
 //
 // How it is computed is this file's own design for gfx950:
-//   * One workgroup (4 waves) per (sequence, kv head, 512-token partition).
+//   * One workgroup (4 waves) per (sequence, kv head, 1024-token partition).
 //     Waves take interleaved 32-token steps of the partition, keep an online
 //     softmax state each, merge in LDS, and the last-arriving workgroup of a
 //     sequence merges the partitions (log-sum-exp identity) and writes out.
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 // kMaxScanSeqs sequences).
 //
 // Every workgroup first scans the context lengths into LDS: per sequence the
-// number of full 512-token partitions and whether a shorter trailing one
+// number of full 1024-token partitions and whether a shorter trailing one
 // follows. The work items -- (sequence, kv head, partition) -- are numbered
 // full partitions first, then the trailing partial ones, so the queue ends
 // with the smallest items. Workgroups take items from an atomic counter in the

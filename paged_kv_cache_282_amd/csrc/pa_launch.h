@@ -9,7 +9,7 @@
 
 namespace pa {
 
-constexpr int kPartition = 512;   // split-K partition (tokens), see PA_DECODE_PARTITION
+constexpr int kPartition = 1024;   // split-K partition (tokens), see PA_DECODE_PARTITION
 constexpr int kWaves = 4;         // waves per workgroup in the attention kernels
 constexpr int kStep = 32;         // tokens per wave step
 

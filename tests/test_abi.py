@@ -63,9 +63,10 @@ def test_status_strings(lib):
 def test_workspace_size(lib):
     f = lib.pa_decode_workspace_size
     assert f(0, 8, 128, 100) == 0
-    a = f(4, 8, 128, 512)
-    b = f(4, 8, 128, 513)   # one more partition
-    c = f(8, 8, 128, 513)
+    P = pa.DECODE_PARTITION
+    a = f(4, 8, 128, P)
+    b = f(4, 8, 128, P + 1)   # one more partition
+    c = f(8, 8, 128, P + 1)
     assert 0 < a < b < c
     # partials for every (seq, head, partition): (d + 2) floats
     assert b >= 4 * 8 * 2 * (128 + 2) * 4

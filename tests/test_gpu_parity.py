@@ -11,6 +11,8 @@ import numpy as np
 import pytest
 import torch
 
+import paged_kv_cache_282_amd as pa
+
 from tests.gpu_helpers import (TOL, DeviceStep, bits, i32, max_err, oracle_decode,
                                oracle_pool_after, oracle_prefill, to_dev, values)
 from tests.pool_writer import unshare_blocks
@@ -78,8 +80,11 @@ def test_float32_at_full_shapes(name):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_shape_matrix(dtype, d, bs, G):
-    """Edge lengths around blocks, steps and the 512-token partition."""
-    lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1024, 1025, 1537]
+    """Edge lengths around blocks, steps, an item's step rounds (4 waves x 32
+    tokens) and the split-K partition."""
+    P = pa.DECODE_PARTITION
+    lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 511, 512, 513,
+            P - 1, P, P + 1, 2 * P, 2 * P + 1, 3 * P - 31]
     w = build_decode_workload("matrix", 1000 + d + bs + G, lens, 2 * G, 2, d, bs, dtype)
     _check_step(w, f"matrix-{dtype}-d{d}-bs{bs}-G{G}")
 
