@@ -70,7 +70,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
                                            0x00020000);
 }
-// Cache-policy bits of a buffer load: nt (nontemporal, streaming).
+// Cache-policy bits of a buffer load: the default (cached), or nt
+// (nontemporal: streamed past the caches).
+constexpr int kCached = 0;
 constexpr int kNontemporal = 2;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -194,6 +196,8 @@ struct Bf16Engine {
 
   // Issue the loads of a 32-token step. Tokens t0..t0+15 live in block blkA
   // and t0+16..t0+31 in blkB (bs 16) or all in blkA (bs 32).
+  // POL is the loads' cache policy (kNontemporal or kCached).
+  template <int POL = kNontemporal>
   __device__ __forceinline__ void load_kv(KV& kv, const uint16_t* __restrict__ pool,
                                           int64_t blk_elems, int64_t kofs, int64_t vofs, int blkA,
                                           int blkB, int lane, bool live = true) const {
@@ -203,9 +207,11 @@ struct Bf16Engine {
     // Each load is a buffer load through a descriptor of one kv head's K or V
     // tile: the tile base is wave-uniform (scalar registers), each lane adds
     // its constant offset and a compile-time displacement, and the hardware
-    // returns zero for anything outside the tile. The loads carry the
-    // nontemporal hint: K/V are read once, and streaming them past the caches
-    // this way sustains a higher HBM read rate on this chip than plain loads.
+    // returns zero for anything outside the tile. K/V read once are best
+    // loaded with the nontemporal hint: streaming them past the caches this
+    // way sustains a higher HBM read rate on this chip than plain loads. K/V
+    // that other sequences of the batch read too (shared blocks) are loaded
+    // cached instead, so those readers find them in the caches.
     const int r = lane & 15, kg = lane >> 4;
     if (!live) blkA = blkB = 0;
     blkA = __builtin_amdgcn_readfirstlane(blkA);
@@ -225,13 +231,13 @@ struct Bf16Engine {
     constexpr int vs = 16 * 8;       // next 16 dims of V
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kv.kA[s] = __builtin_amdgcn_raw_buffer_load_b128(kra, ko + ks * s, 0, kNontemporal);
-      kv.kB[s] = __builtin_amdgcn_raw_buffer_load_b128(krb, ko + kb + ks * s, 0, kNontemporal);
+      kv.kA[s] = __builtin_amdgcn_raw_buffer_load_b128(kra, ko + ks * s, 0, POL);
+      kv.kB[s] = __builtin_amdgcn_raw_buffer_load_b128(krb, ko + kb + ks * s, 0, POL);
     }
 #pragma unroll
     for (int j = 0; j < VT; ++j) {
-      const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(vra, vo + vs * j, 0, kNontemporal);
-      const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(vrb, vo + vb + vs * j, 0, kNontemporal);
+      const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(vra, vo + vs * j, 0, POL);
+      const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(vrb, vo + vb + vs * j, 0, POL);
       kv.vv[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   }
@@ -648,11 +654,14 @@ struct ScanSmem {
   int n[kMaxScanSeqs];         // clamped context length
   int wsum[kWaves][2];
   int item;
+  unsigned long long tokens;  // sum of the clamped context lengths
+  int shared;                 // some sequence starts with its predecessor's first block
 };
 
+// A context length as the kernels use it: at least 0, at most max_ctx and at
+// most what the table row can address.
 template <int BS>
-__device__ __forceinline__ int clamped_len(const DecodeArgs& a, int b) {
-  int n = a.lens[b];
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int n) {
   n = n < 0 ? 0 : n;
   n = n > a.max_ctx ? a.max_ctx : n;
   return n > a.mb * BS ? a.mb * BS : n;
@@ -772,44 +781,62 @@ __device__ __forceinline__ void leave_queue(int32_t* __restrict__ queue) {
   }
 }
 
-// The whole decode pipeline of one workgroup: takes items until the queue
-// runs past the last one. Every workgroup of the grid runs it.
+// K+V bytes of a call up to which its loads stay cached: a batch this small
+// may still be in the 256 MiB last-level cache when it is read again.
+constexpr uint64_t kCachedCallBytes = 256ull << 20;
+
+// Every workgroup scans the context lengths into LDS and takes its first two
+// queue items. Returns whether the call's K/V loads should stay cached: when
+// some sequence's first block is also its predecessor's (parallel samples or
+// a cached prefix: the blocks are read again by the other sequences), or when
+// the call reads little enough for the caches to hold it.
 template <int D, int BS>
-__device__ __forceinline__ void decode_persistent(const DecodeArgs& a, int32_t* __restrict__ queue,
-                                                  DecodeSmem<D>& ds) {
-  using Eng = Bf16Engine<D, BS, 1>;
-  constexpr int KS = Eng::KS;
-  constexpr int kSteps = kPartition / (kWaves * kStep);  // steps per wave per partition
-  static_assert(kSteps % 2 == 0, "steps alternate between two register buffers");
-  MergeSmem<D>(&sm2)[2] = ds.sm2;
+__device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __restrict__ queue,
+                                            DecodeSmem<D>& ds) {
   ScanSmem& sc = ds.sc;
   int(&s_next)[2] = ds.s_next;
   const int B = a.num_seqs;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15, kg = lane >> 4;
-  const int G = a.hq / a.hkv;
-  const uint16_t* pool = static_cast<const uint16_t*>(a.pool);
-  const uint16_t* q = static_cast<const uint16_t*>(a.q);
-
-  // -- scan the lengths; take the first two items ---------------------------------
   {
     constexpr int kPer = kMaxScanSeqs / 256;
     const int per = (B + 255) / 256;
     int nl[kPer];
-    int fx = 0, py = 0;
+    int fx = 0, py = 0, shared = 0;
+    uint64_t tok = 0;
+    // The first table entries are loaded together with the lengths (never
+    // behind them), so the scan waits for one round trip to memory.
+    int first[kPer], before[kPer];
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
       const int i = threadIdx.x * per + c;
       nl[c] = 0;
+      first[c] = -1;
+      before[c] = -2;
       if (c < per && i < B) {
-        nl[c] = clamped_len<BS>(a, i);
-        fx += nl[c] / kPartition;
-        py += (nl[c] % kPartition != 0 || nl[c] == 0) ? 1 : 0;
+        nl[c] = a.lens[i];
+        first[c] = a.tables[static_cast<int64_t>(i) * a.mb];
+        if (i > 0) before[c] = a.tables[static_cast<int64_t>(i - 1) * a.mb];
       }
     }
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int i = threadIdx.x * per + c;
+      if (c < per && i < B) {
+        nl[c] = clamp_len<BS>(a, nl[c]);
+        fx += nl[c] / kPartition;
+        py += (nl[c] % kPartition != 0 || nl[c] == 0) ? 1 : 0;
+        tok += static_cast<uint64_t>(nl[c]);
+        shared |= (nl[c] > 0 && first[c] == before[c] &&
+                   static_cast<uint32_t>(first[c]) < static_cast<uint64_t>(a.nb)) ? 1 : 0;
+      }
+    }
+    if (threadIdx.x == 0) {
+      sc.tokens = 0;
+      sc.shared = 0;
+    }
     int ex, ey, tx, ty;
-    block_scan2(sc, fx, py, ex, ey, tx, ty);
+    block_scan2(sc, fx, py, ex, ey, tx, ty);  // (its barrier also orders the clears)
+    if (tok != 0) atomicAdd(&sc.tokens, static_cast<unsigned long long>(tok));
+    if (shared) atomicOr(&sc.shared, 1);
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
       const int i = threadIdx.x * per + c;
@@ -829,6 +856,30 @@ __device__ __forceinline__ void decode_persistent(const DecodeArgs& a, int32_t* 
     }
     __syncthreads();
   }
+  const uint64_t bytes = sc.tokens * static_cast<uint64_t>(a.hkv) * 2 * D * 2;
+  return __builtin_amdgcn_readfirstlane(sc.shared != 0 || bytes <= kCachedCallBytes) != 0;
+}
+
+// The decode pipeline of one workgroup after the scan: takes items until the
+// queue runs past the last one. POL is the cache policy of the K/V loads.
+template <int D, int BS, int POL>
+__device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __restrict__ queue,
+                                            DecodeSmem<D>& ds) {
+  using Eng = Bf16Engine<D, BS, 1>;
+  constexpr int KS = Eng::KS;
+  constexpr int kSteps = kPartition / (kWaves * kStep);  // steps per wave per partition
+  static_assert(kSteps % 2 == 0, "steps alternate between two register buffers");
+  MergeSmem<D>(&sm2)[2] = ds.sm2;
+  ScanSmem& sc = ds.sc;
+  int(&s_next)[2] = ds.s_next;
+  const int B = a.num_seqs;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, kg = lane >> 4;
+  const int G = a.hq / a.hkv;
+  const uint16_t* pool = static_cast<const uint16_t*>(a.pool);
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+
   const int n_full_items = sc.full[B] * a.hkv;
   const int total = n_full_items + sc.part[B] * a.hkv;
 
@@ -887,7 +938,8 @@ __device__ __forceinline__ void decode_persistent(const DecodeArgs& a, int32_t* 
     const int64_t vofs =
         static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(pl.it.g) * D * BS;
     const bool live = pl.it.tok0 + kStep * (wave + kWaves * s2) < pl.it.tok1;
-    eng.load_kv(buf, pool, a.blk_elems, kofs, vofs, pl.idA[s2], pl.idB[s2], lane, live);
+    eng.template load_kv<POL>(buf, pool, a.blk_elems, kofs, vofs, pl.idA[s2], pl.idB[s2], lane,
+                              live);
   };
 
   // The wave states of item i are merged and published while item i+1's
@@ -969,6 +1021,17 @@ __device__ __forceinline__ void decode_persistent(const DecodeArgs& a, int32_t* 
     nxt_k = after_k;
   }
   if (have_prev) publish(sm2[parity ^ 1], prev);
+}
+
+// The whole decode of one workgroup: scan, then the loop under the call's
+// cache policy (the same in every workgroup: it depends only on the inputs).
+template <int D, int BS>
+__device__ __forceinline__ void decode_persistent(const DecodeArgs& a, int32_t* __restrict__ queue,
+                                                  DecodeSmem<D>& ds) {
+  if (decode_scan<D, BS>(a, queue, ds))
+    decode_loop<D, BS, kCached>(a, queue, ds);
+  else
+    decode_loop<D, BS, kNontemporal>(a, queue, ds);
 }
 
 template <int D, int BS>
@@ -1578,14 +1641,21 @@ inline int compute_units() {
 template <int D, int BS>
 hipError_t launch_decode_bf16(const DecodeArgs& a, int grid, int32_t* queue, hipStream_t st) {
   if (a.num_seqs <= kMaxScanSeqs) {
-    // One workgroup per compute unit. Two fit, but each wave keeps two 16 KiB
-    // steps in flight, and at two workgroups per unit the loads in flight
-    // (about 64 MiB) only lengthen the queueing latency of every load without
-    // raising the HBM rate; the longer latency then stretches the tail, where
-    // the last items of each workgroup wait out one latency each. Measured on
-    // the GQA long-tail batch: 244.8 us at two per unit, 239.5 us at one.
+    // Two workgroups fit on a compute unit. A long batch (more than 16
+    // possible items per unit) runs one per unit instead: each wave keeps two
+    // 16 KiB steps in flight, and once HBM is the bound, the loads of a second
+    // workgroup (about 64 MiB in flight in all) only lengthen the queueing
+    // latency of every load; the tail, where each workgroup waits out its
+    // last items, stretches with it. Shorter batches keep two per unit: their
+    // loads are fewer or, with shared prefix blocks, largely served by the
+    // caches, and there more loads in flight pay. Measured: GQA long-tail
+    // batch 244.8 -> 239.5 us and MHA batch 189.3 -> 184.6 us with one per
+    // unit; shared-prefix batch 188 us with two per unit, 219 us with one.
+    static const int resident = resident_workgroups(decode_bf16_persistent_kernel<D, BS>);
     static const int cus = compute_units();
-    const int w = min(grid, cus > 0 ? cus : 256);
+    const int units = cus > 0 ? cus : 256;
+    const bool long_batch = static_cast<int64_t>(grid) > 16LL * units;
+    const int w = min(grid, long_batch ? units : (resident > 0 ? resident : 2 * units));
     hipLaunchKernelGGL((decode_bf16_persistent_kernel<D, BS>), dim3(w), dim3(256), 0, st, a,
                        queue);
   } else {
