@@ -216,6 +216,31 @@ def test_batch_composition_is_bit_invariant():
     assert np.array_equal(bits(out), full[order])
 
 
+@pytest.mark.parametrize("d,bs", [(64, 16), (64, 32), (128, 32)])
+def test_long_batch_paths_match_short_batch_bitwise(d, bs):
+    """A long batch (more than 256 MiB of K+V, more than 16 possible items per
+    compute unit, no shared blocks) runs one workgroup per unit with streaming
+    (nontemporal) loads; a short one runs two per unit with cached loads. Both
+    must give the oracle's result, and each sequence the same bits either way."""
+    rng = np.random.default_rng(7000 + d + bs)
+    lens = rng.integers(1100, 2101, 1024)
+    w = build_decode_workload("long", 7100 + d + bs, lens, 8, 2, d, bs, "bf16")
+    kv_bytes = int(lens.sum()) * 2 * 2 * d * 2
+    assert kv_bytes > (256 << 20)
+    assert len(lens) * 2 * -(-int(lens.max()) // pa.DECODE_PARTITION) > 16 * 256
+    st = _check_step(w, f"long-d{d}-bs{bs}")
+    full = bits(st.out).copy()
+    order = np.array([5, 0, 1023, 200, 5])
+    sub = torch.from_numpy(order).cuda()
+    out = torch.empty((len(order), w.num_q_heads, w.head_dim), dtype=st.q.dtype, device="cuda")
+    sub_max = int(w.context_lens[order].max())
+    pa.pa_decode(out, st.q[sub].contiguous(), st.pool, st.tables[sub].contiguous(),
+                 st.lens[sub].contiguous(), sub_max, w.num_kv_heads, w.block_size, w.scale,
+                 pa.new_decode_workspace(len(order), w.num_q_heads, w.head_dim, sub_max))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), full[order])
+
+
 def test_prefill_chunk_of_one_matches_decode():
     w = make_workload("mixed", num_decode=2, dec_max=300, num_chunks=6, chunk_len=1,
                       max_prior=1500, num_q_heads=8, num_kv_heads=2)
