@@ -1235,7 +1235,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
   const int64_t vofs = static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(g) * D * BS;
 
   // Piece p of a step: K pieces first ([slice c][token t], one token's 8
-  // dims), then V pieces ([4-token slice s][dim pair], 2 dims x 4 tokens).
+  // dims), then V pieces: 2 dims x 4 tokens of one 4-token slice, where
+  // V piece 2m + h is dim pair m % (D/2) of slice pair m / (D/2), set h
+  // (a: tokens 4c.., b: tokens 16+4c..). Adjacent lanes thus hold the two sets
+  // of the same two dims, which the stash turns into two whole LDS rows.
   // Returns the element offset inside the step's block (A: tokens 0..15 or,
   // at bs 32, all 32) and whether it comes from block B (bs 16, tokens 16..31).
   auto piece_src = [&](int pc, bool& from_b) -> int64_t {
@@ -1246,7 +1249,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
       return kofs + (static_cast<int64_t>(sl) * BS + slot) * 8;
     }
     const int pv = pc - kChunks / 2;
-    const int sl = pv / (D / 2), dp = pv - sl * (D / 2);
+    const int m = pv >> 1;
+    const int cp = m / (D / 2), dp = m - cp * (D / 2);
+    const int sl = cp + 4 * (pv & 1);
     from_b = BS == 16 && sl >= 4;
     const int bsl = BS == 16 ? (sl & 3) : sl;
     return vofs + (static_cast<int64_t>(bsl) * D + 2 * dp) * 4;
@@ -1277,10 +1282,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
       const int pc = u * 256 + static_cast<int>(threadIdx.x);
       if (pc < kChunks / 2) {
         *reinterpret_cast<u32x4*>(&lk[buf * kK + pc * 8]) = pre[u];
-      } else {  // 4 tokens of dims 2dp and 2dp+1 of 4-token slice sl, 8 bytes each
+      } else {
+        // 4 tokens of dims 2dp and 2dp+1 of set `odd` of slice pair cp, 8
+        // bytes each. Adjacent lanes hold the two sets of the same dims, so
+        // each store instruction fills whole 16-byte rows pairwise (a 2-way
+        // bank pattern; one lane per row pair would be 8-way).
         const int pv = pc - kChunks / 2;
-        const int sl = pv / (D / 2), dp = pv - sl * (D / 2);
-        uint16_t* row = &lv[buf * kV + ((sl & 3) * D + 2 * dp) * 8 + (sl >> 2) * 4];
+        const int m = pv >> 1, odd = pv & 1;
+        const int cp = m / (D / 2), dp = m - cp * (D / 2);
+        uint16_t* row = &lv[buf * kV + (cp * D + 2 * dp) * 8 + odd * 4];
         *reinterpret_cast<u32x2*>(row) = u32x2{pre[u][0], pre[u][1]};
         *reinterpret_cast<u32x2*>(row + 8) = u32x2{pre[u][2], pre[u][3]};
       }
