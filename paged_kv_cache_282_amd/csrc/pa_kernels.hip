@@ -11,17 +11,20 @@
 //     section "The prefill/decode mix": prefill chunks in the same iteration.
 //
 // How it is computed is this file's own design for gfx950:
-//   * One workgroup (4 waves) per (sequence, kv head, 1024-token partition).
-//     Waves take interleaved 32-token steps of the partition, keep an online
-//     softmax state each, merge in LDS, and the last-arriving workgroup of a
-//     sequence merges the partitions (log-sum-exp identity) and writes out.
+//   * Decode works on items (sequence, kv head, 1024-token partition) that a
+//     persistent grid takes from a queue; a workgroup's four waves take
+//     interleaved 32-token steps of an item, keep an online softmax state
+//     each and merge in LDS. A sequence of several partitions publishes one
+//     partial per partition, and a second kernel merges them (log-sum-exp
+//     identity). The grid size and the loads' cache policy follow the batch.
 //   * bf16: scores and p.V run on v_mfma_f32_16x16x32_bf16. The 16 columns of
 //     each MFMA are the query heads of one GQA group (padded) or, in prefill,
 //     (position, head) rows. The pool keeps K in 8-element slices and V in
 //     4-token slices, so every MFMA operand is one contiguous load and each
 //     lane's eight scores are exactly the eight tokens whose V values the same
 //     lane holds for p.V: probabilities never leave registers. Every load
-//     instruction reads a single block through a uniform base address.
+//     instruction reads a single block through a uniform base address
+//     (decode: a buffer descriptor of one kv head's K or V tile).
 //   * Tokens outside a context are excluded by selection (-inf scores, zeroed
 //     V), never by multiplying with p = 0, so NaN in unused slots is harmless.
 //   * fp32: a VALU kernel with the same work decomposition (16 lanes per token
