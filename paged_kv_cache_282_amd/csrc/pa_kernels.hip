@@ -1654,21 +1654,17 @@ inline int compute_units() {
 template <int D, int BS>
 hipError_t launch_decode_bf16(const DecodeArgs& a, int grid, int32_t* queue, hipStream_t st) {
   if (a.num_seqs <= kMaxScanSeqs) {
-    // Two workgroups fit on a compute unit. A long batch (more than 16
-    // possible items per unit) runs one per unit instead: each wave keeps two
-    // 16 KiB steps in flight, and once HBM is the bound, the loads of a second
-    // workgroup (about 64 MiB in flight in all) only lengthen the queueing
-    // latency of every load; the tail, where each workgroup waits out its
-    // last items, stretches with it. Shorter batches keep two per unit: their
-    // loads are fewer or, with shared prefix blocks, largely served by the
-    // caches, and there more loads in flight pay. Measured: GQA long-tail
-    // batch 244.8 -> 239.5 us and MHA batch 189.3 -> 184.6 us with one per
-    // unit; shared-prefix batch 188 us with two per unit, 219 us with one.
-    static const int resident = resident_workgroups(decode_bf16_persistent_kernel<D, BS>);
+    // One workgroup per compute unit, although two fit. Each wave keeps two
+    // 16 KiB steps in flight; with a second workgroup per unit (about 64 MiB
+    // in flight on an HBM-bound batch) the extra loads only lengthen the
+    // queueing latency of every load, and the tail, where each workgroup waits
+    // out its last items, stretches with it. Cached batches (shared prefixes,
+    // small calls) gain from one per unit too. Measured, two per unit -> one:
+    // GQA long-tail batch 244.8 -> 239.5 us, MHA batch 185.6 -> 181.6 us,
+    // shared-prefix batch 192.8 -> 184.9 us, engine loop (paged) 1.44 -> 1.49 M
+    // tokens/s.
     static const int cus = compute_units();
-    const int units = cus > 0 ? cus : 256;
-    const bool long_batch = static_cast<int64_t>(grid) > 16LL * units;
-    const int w = min(grid, long_batch ? units : (resident > 0 ? resident : 2 * units));
+    const int w = min(grid, cus > 0 ? cus : 256);
     hipLaunchKernelGGL((decode_bf16_persistent_kernel<D, BS>), dim3(w), dim3(256), 0, st, a,
                        queue);
   } else {

@@ -218,10 +218,10 @@ def test_batch_composition_is_bit_invariant():
 
 @pytest.mark.parametrize("d,bs", [(64, 16), (64, 32), (128, 32)])
 def test_long_batch_paths_match_short_batch_bitwise(d, bs):
-    """A long batch (more than 256 MiB of K+V, more than 16 possible items per
-    compute unit, no shared blocks) runs one workgroup per unit with streaming
-    (nontemporal) loads; a short one runs two per unit with cached loads. Both
-    must give the oracle's result, and each sequence the same bits either way."""
+    """A long batch (more than 256 MiB of K+V, no shared blocks) streams its
+    K/V with nontemporal loads; a short one loads them cached. Both must give
+    the oracle's result, and each sequence the same bits either way. (The long
+    batch also exceeds 16 possible items per compute unit.)"""
     rng = np.random.default_rng(7000 + d + bs)
     lens = rng.integers(1100, 2101, 1024)
     w = build_decode_workload("long", 7100 + d + bs, lens, 8, 2, d, bs, "bf16")
