@@ -1527,12 +1527,18 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 // KV append and block copy (pure data movement).
 // ---------------------------------------------------------------------------
-// Thread -> (token, kv head, 8-element slice). K: the slice is one contiguous
-// 8-element run. V: the slice's 8 dimensions sit 4 elements apart in the
-// token's 4-slot slice. When four consecutive tokens of the list fill one
-// whole 4-slot slice (a prefill chunk does), the first of them writes the
-// slice's 8 dimensions for all four tokens as one contiguous run and the other
-// three write no V; otherwise each token writes its own V elements.
+// Wave -> (16 consecutive tokens of the list, kv head, 4 consecutive
+// 8-element slices); lane -> (token lane/4, slice lane%4), so the four lanes
+// of a token read 64 contiguous bytes of its row. Each lane loads its slot and
+// its K and V slice in one round trip. K: the slice is one contiguous
+// 8-element run at its slot, so lanes of consecutive slots write consecutive
+// 16-byte pieces. V: the slice's 8 dimensions sit 4 elements apart in the
+// token's 4-slot slice. When the four tokens holding slots 4j .. 4j+3 of one
+// block are all in the wave (a prefill chunk's consecutive tokens are), the
+// lane of the token at slot 4j+i gathers dimension pair i of all four tokens
+// from the other three with lane shuffles and writes it as one contiguous
+// piece, so the four write the slice's whole 8-dimension run; otherwise each
+// lane writes its own token's V elements.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void append_kernel(T* __restrict__ pool,
                                                      const T* __restrict__ kn,
@@ -1541,62 +1547,98 @@ __global__ __launch_bounds__(256) void append_kernel(T* __restrict__ pool,
                                                      int num_tokens, int hkv, int bs,
                                                      int64_t blk_elems, int64_t num_slots) {
   constexpr int CH = D / 8;
-  constexpr int E16 = 16 / sizeof(T);  // elements per 16-byte word
-  constexpr int W = 8 / E16;           // 16-byte words per 8-element slice
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t per_tok = static_cast<int64_t>(hkv) * CH;
-  const int64_t tok = gid / per_tok;
-  if (tok >= num_tokens) return;
-  const int rem = static_cast<int>(gid - tok * per_tok);
-  const int h = rem / CH, ch = rem - h * CH;
-  const int slot = slots[tok];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / bs;
-  const int off = slot - static_cast<int>(blk) * bs;
+  constexpr int E16 = 16 / sizeof(T);    // elements per 16-byte word
+  constexpr int W = 8 / E16;             // 16-byte words per 8-element slice
+  constexpr int WPP = sizeof(T) / 2;     // 32-bit words per dimension pair
+  constexpr int CG = CH / 4;             // groups of 4 slices
+  static_assert(CH % 4 == 0, "a wave takes 4 slices of each token");
+  const int lane = threadIdx.x & 63;
+  const int tl = lane >> 2, cl = lane & 3;  // token and slice within the wave
+  const int64_t wid = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+  const int64_t per_blk = static_cast<int64_t>(hkv) * CG;
+  const int64_t tb = wid / per_blk;
+  const int rem = static_cast<int>(wid - tb * per_blk);
+  const int h = rem / CG, ch = (rem - h * CG) * 4 + cl;
+  const int64_t tok = tb * 16 + tl;
+  const bool in = tok < num_tokens;
+  // one round trip: the slot and this token's K and V slice
+  const int64_t src = ((in ? tok : 0) * hkv + h) * D + ch * 8;
+  u32x4 kw[W], vw[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    kw[w] = ld16(kn + src + w * E16);
+    vw[w] = ld16(vn + src + w * E16);
+  }
+  const int slot = in ? slots[tok] : -1;
+  const bool valid = slot >= 0 && slot < num_slots;
+  const int64_t blk = valid ? slot / bs : 0;
+  const int off = valid ? slot - static_cast<int>(blk) * bs : 0;
   const int64_t tile = static_cast<int64_t>(h) * bs * D;
-  // K: slice ch of slot off
-  {
-    const int64_t src = (tok * hkv + h) * D + ch * 8;
+  if (valid) {
     T* kd = pool + blk * blk_elems + tile + (static_cast<int64_t>(ch) * bs + off) * 8;
 #pragma unroll
-    for (int w = 0; w < W; ++w) st16(kd + w * E16, ld16(kn + src + w * E16));
+    for (int w = 0; w < W; ++w) st16(kd + w * E16, kw[w]);
   }
-  // V: dims ch*8 .. +7 of the 4-slot slice off/4
+  // V. The tokens of one 4-slot slice: base .. base+3 of the wave with
+  // base = tl - off%4. Every lane runs the shuffles (clamped indices); the
+  // slice is whole iff those four tokens hold its four slots in order, which
+  // all four lanes then see.
+  const int r = off & 3;
+  const int base = tl - r;
+  bool quad = valid && base >= 0 && base + 3 < 16;
+  uint32_t words[4 * W];  // this lane's 8 dimensions as 32-bit words
+#pragma unroll
+  for (int w = 0; w < W; ++w)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) words[4 * w + x] = vw[w][x];
+  uint32_t g[4][WPP] = {};  // dimension pair r of tokens base .. base+3
+  // Waves whose slots never run on (a decode step's one token per sequence)
+  // skip the shuffles: the test is uniform over the wave.
+  const int next_slot = __shfl(slot, min(lane + 4, 63));  // the next token, same slice
+  if (__builtin_amdgcn_ballot_w64(valid && tl < 15 && next_slot == slot + 1) != 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int from = min(max(base + j, 0), 15) * 4 + cl;
+      quad = quad && __shfl(slot, from) == slot - r + j;
+#pragma unroll
+      for (int x = 0; x < WPP; ++x) {
+        // the word of dimension pair r sits at index r*WPP + x of the
+        // sender; every lane asks for its own r, so all four candidates are
+        // gathered and the lane picks its own
+        uint32_t pick = 0;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const uint32_t c =
+              static_cast<uint32_t>(__shfl(static_cast<int>(words[rr * WPP + x]), from));
+          pick = (rr == r) ? c : pick;
+        }
+        g[j][x] = pick;
+      }
+    }
+  } else {
+    quad = false;
+  }
   T* vslice = pool + blk * blk_elems + static_cast<int64_t>(hkv) * bs * D + tile +
               (static_cast<int64_t>(off / 4) * D + ch * 8) * 4;
-  const int r = off & 3;
-  const int64_t lead = tok - r;  // the token that would hold slot (slot - r)
-  bool quad = lead >= 0 && lead + 3 < num_tokens;
   if (quad) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) quad = quad && slots[lead + k] == slot - r + k;
-  }
-  if (quad) {
-    if (r != 0) return;  // the slice's first token writes it
-    T v[4][8];           // [token][dim]
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t src = ((tok + k) * hkv + h) * D + ch * 8;
-#pragma unroll
-      for (int w = 0; w < W; ++w)
-        *reinterpret_cast<u32x4*>(&v[k][w * E16]) = ld16(vn + src + w * E16);
+    // dims 2r and 2r+1 of the four tokens: [dim 2r: t0 t1 t2 t3][dim 2r+1: t0 .. t3]
+    T* dst = vslice + 8 * r;  // vslice is slot position 0 of dimension ch*8
+    if constexpr (sizeof(T) == 2) {
+      u32x4 o;
+      o[0] = (g[0][0] & 0xFFFFu) | (g[1][0] << 16);
+      o[1] = (g[2][0] & 0xFFFFu) | (g[3][0] << 16);
+      o[2] = (g[0][0] >> 16) | (g[1][0] & 0xFFFF0000u);
+      o[3] = (g[2][0] >> 16) | (g[3][0] & 0xFFFF0000u);
+      st16(dst, o);
+    } else {
+      st16(dst, u32x4{g[0][0], g[1][0], g[2][0], g[3][0]});
+      st16(dst + 4, u32x4{g[0][1], g[1][1], g[2][1], g[3][1]});
     }
-    T t[8][4];  // [dim][token]: the slice's layout
+  } else if (valid) {
+    const T* v = reinterpret_cast<const T*>(words);
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) t[e][k] = v[k][e];
-    const T* tw = &t[0][0];
-#pragma unroll
-    for (int w = 0; w < 4 * W; ++w) st16(vslice + w * E16, *reinterpret_cast<const u32x4*>(tw + w * E16));
-    return;
+    for (int e = 0; e < 8; ++e) vslice[4 * e + r] = v[e];
   }
-  const int64_t src = (tok * hkv + h) * D + ch * 8;
-  T v[8];
-#pragma unroll
-  for (int w = 0; w < W; ++w) *reinterpret_cast<u32x4*>(&v[w * E16]) = ld16(vn + src + w * E16);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) vslice[4 * e + r] = v[e];
 }
 
 // Whole blocks from one pool to another (the same one for copy-on-write; the
@@ -1735,7 +1777,9 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, int max_chunk_len, hipStream
 hipError_t launch_append(void* pool, const void* k_new, const void* v_new, const int32_t* slots,
                          int num_tokens, const PoolShape& ps, int dtype, hipStream_t st) {
   if (num_tokens == 0) return hipSuccess;
-  const int64_t threads = static_cast<int64_t>(num_tokens) * ps.num_kv_heads * (ps.head_dim / 8);
+  // a wave per (16 tokens, kv head, 4 slices of 8 elements)
+  const int64_t threads =
+      (static_cast<int64_t>(num_tokens) + 15) / 16 * 64 * ps.num_kv_heads * (ps.head_dim / 32);
   const int grid = static_cast<int>((threads + 255) / 256);
   const int64_t num_slots = ps.num_blocks * ps.block_size;
   const int64_t be = ps.block_elems();
