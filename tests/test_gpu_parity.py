@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import paged_kv_cache_282_amd as pa
 
 from tests.gpu_helpers import (TOL, DeviceStep, bits, i32, max_err, oracle_decode,
@@ -239,6 +240,44 @@ def test_long_batch_paths_match_short_batch_bitwise(d, bs):
                  pa.new_decode_workspace(len(order), w.num_q_heads, w.head_dim, sub_max))
     torch.cuda.synchronize()
     assert np.array_equal(bits(out), full[order])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d,bs", [(64, 16), (128, 32)])
+def test_append_slot_patterns_bit_exact(dtype, d, bs):
+    """Slot lists that exercise every branch of the append: a long run that
+    starts mid-slice and crosses block and wave boundaries, a run with padding
+    (-1) tokens inside it, a run in reverse order, isolated slots, and a run
+    that starts on a slice boundary. The pool must equal the oracle's bit for
+    bit (unused slots hold NaN, so a stray write shows)."""
+    rng = np.random.default_rng(9000 + d + bs)
+    hkv, nb = 2, 24
+    run_a = list(range(3 * bs + 5, 3 * bs + 5 + 70))          # mid-slice start, 70 long
+    run_b = list(range(9 * bs + 2, 9 * bs + 2 + 41))
+    run_b[2] = -1
+    run_b[37] = -1                                            # padding inside a run
+    run_c = list(range(14 * bs + 19, 14 * bs + 1, -1))[:18]   # descending slots
+    iso = [17 * bs + 3, 18 * bs + 11, 19 * bs + 7, 20 * bs]   # one token per block
+    run_e = list(range(21 * bs, 21 * bs + 24))                # starts on a slice
+    slots = np.array(run_a + run_b + run_c + iso + run_e, np.int64)
+    used = slots[slots >= 0]
+    assert len(np.unique(used)) == len(used) and used.max() < nb * bs
+    n = len(slots)
+    elems = nb * 2 * hkv * bs * d
+    f = rng.standard_normal(elems).astype(np.float32)
+    f[rng.random(elems) < 0.5] = np.nan
+    kf = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    vf = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    if dtype == "bf16":
+        pool, k_new, v_new = [(x.view(np.uint32) >> 16).astype(np.uint16) for x in (f, kf, vf)]
+    else:
+        pool, k_new, v_new = f, kf, vf
+    pool = pool.reshape(nb, 2 * hkv * bs * d)
+    want = oracle.append(pool, k_new, v_new, slots, hkv, bs, d)
+    dpool = to_dev(pool, dtype)
+    pa.pa_append_kv(dpool, to_dev(k_new, dtype), to_dev(v_new, dtype), i32(slots), bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(dpool).view(np.uint8), want.view(np.uint8))
 
 
 def test_prefill_chunk_of_one_matches_decode():
