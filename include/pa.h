@@ -138,7 +138,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  *   out           [num_seqs][num_q_heads][head_dim]  (must not overlap q)
  *   q             [num_seqs][num_q_heads][head_dim]
  *   block_tables  [num_seqs][max_blocks_per_seq] int32 physical block ids;
- *                 entries at or past ceil(n/bs) are never read.
+ *                 entries at or past ceil(n/bs) never address the pool (entry
+ *                 0 of every row is read to choose the cache policy below,
+ *                 whatever it holds).
  *   context_lens  [num_seqs] int32: sequence b attends to its logical tokens
  *                 0 .. context_lens[b]-1 (including a token appended this
  *                 step). A zero length gives a zero output row. Slots past
@@ -154,6 +156,10 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  *                 workspaces.
  * Sequences longer than PA_DECODE_PARTITION are split into partitions whose
  * partial softmax states are merged by a second kernel on the same stream.
+ * Cache behaviour: a call whose K+V exceeds 256 MiB and in which no sequence
+ * starts with its predecessor's first block streams K/V with nontemporal
+ * loads (they are not kept in the caches); other calls load them cached. The
+ * results are bit-identical either way.
  */
 int pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
               const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
