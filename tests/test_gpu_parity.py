@@ -280,6 +280,37 @@ def test_append_slot_patterns_bit_exact(dtype, d, bs):
     assert np.array_equal(bits(dpool).view(np.uint8), want.view(np.uint8))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_batch_over_2048_sequences(dtype):
+    """More sequences than the persistent decode's scan holds (2048): the call
+    runs one workgroup per (sequence, kv head, partition) instead. Sampled rows
+    against the oracle (every multi-partition sequence among them), and bit
+    for bit against the same sequences decoded in a short batch, which takes
+    the persistent path."""
+    rng = np.random.default_rng(9100)
+    lens = rng.integers(1, 1301, 2100)
+    w = build_decode_workload("over2048", 9101, lens, 4, 2, 64, 16, dtype)
+    st = DeviceStep(w)
+    st.run()
+    want_pool = oracle_pool_after(w)
+    assert np.array_equal(bits(st.pool).view(np.uint8), want_pool.view(np.uint8))
+    long_ = np.flatnonzero(lens > pa.DECODE_PARTITION)
+    idx = np.unique(np.concatenate([rng.choice(len(lens), 48, replace=False), long_[:16],
+                                    [0, len(lens) - 1]]))
+    err = max_err(values(st.out)[idx], oracle_decode(w, want_pool, idx))
+    assert err <= TOL[dtype]
+    full = bits(st.out).copy()
+    order = np.array([long_[0], 7, len(lens) - 1, long_[-1]])
+    sub = torch.from_numpy(order).cuda()
+    out = torch.empty((len(order), w.num_q_heads, w.head_dim), dtype=st.q.dtype, device="cuda")
+    sub_max = int(w.context_lens[order].max())
+    pa.pa_decode(out, st.q[sub].contiguous(), st.pool, st.tables[sub].contiguous(),
+                 st.lens[sub].contiguous(), sub_max, w.num_kv_heads, w.block_size, w.scale,
+                 pa.new_decode_workspace(len(order), w.num_q_heads, w.head_dim, sub_max))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), full[order])
+
+
 def test_prefill_chunk_of_one_matches_decode():
     w = make_workload("mixed", num_decode=2, dec_max=300, num_chunks=6, chunk_len=1,
                       max_prior=1500, num_q_heads=8, num_kv_heads=2)
