@@ -4,8 +4,9 @@ Per item, the fused launch runs the same decode and prefill code as
 pa_decode and pa_prefill_chunk, so its outputs must equal theirs bit for bit;
 they are also checked against the oracle. Cases cover the fused bf16 path at
 small and full size (the mixed continuous-batching iteration: 240 decode
-sequences and 16 chunks of 512 queries), the fp32 path (two launches in
-turn), one-sided calls, and repeated calls that reuse the workspace counters.
+sequences and 16 chunks of 512 queries), the fp32 path and the bf16 batches
+the fused launch does not take (two launches in turn), one-sided calls, and
+repeated calls that reuse the workspace counters.
 """
 import numpy as np
 import pytest
@@ -74,6 +75,20 @@ def test_mixed_full_size_iteration():
                           w.prefill_context_lens[:1], w.query_start_loc[:2], w.num_kv_heads,
                           w.block_size, w.scale, w.dtype)
     assert max_err(values(pout)[:L0], want) <= TOL["bf16"]
+
+
+def test_mixed_bf16_fallbacks_match_separate_calls():
+    """bf16 batches the fused launch does not take run the two launches in
+    turn: more than 1024 prefill tiles (70 chunks of 512 queries at G = 4 are
+    1120 tiles of 32 positions), and more than 2048 decode sequences."""
+    w = make_workload("mixed", seed=88, num_decode=20, dec_min=1, dec_max=900, num_chunks=70,
+                      chunk_len=512, max_prior=64, num_q_heads=8, num_kv_heads=2)
+    assert len(w.prefill_context_lens) * (512 // 32) > 1024
+    _run_both(w, "mixed-many-tiles", oracle_check=False, repeats=1)
+    w = make_workload("mixed", seed=89, num_decode=2100, dec_min=1, dec_max=300, num_chunks=2,
+                      chunk_len=40, max_prior=100, num_q_heads=8, num_kv_heads=2)
+    assert w.num_seqs > 2048
+    _run_both(w, "mixed-many-seqs", oracle_check=False, repeats=1)
 
 
 def test_mixed_one_sided_calls():
