@@ -3,11 +3,12 @@
  *
  * The operations follow the pages this library is built from:
  *   - "Module 4 · Batching, Scheduling, and Paging" (datasystem.school),
- *     section "PagedAttention": each sequence's KV cache is split into
- *     fixed-size blocks stored non-contiguously, with a per-sequence block
- *     table mapping logical blocks to physical ones; attention gathers K and V
- *     through that indirection. Section "Block sharing": a shared prefix block
- *     is copied on the first divergent write.
+ *     section "PagedAttention": a sequence's cache lives in equal-sized
+ *     blocks scattered over one pool, and a table per sequence names the
+ *     physical block behind each of its logical blocks, so attention reads K
+ *     and V by looking each block up in that table. Section "Block sharing":
+ *     before a sample writes into a block it shares with other samples, the
+ *     block is duplicated.
  *   - "Paging the KV Cache" (lecture 6), section "The waste hiding inside
  *     memory": the cache grows token by token.
  *   - worksonmygpu.com continuous-batching post, section "Selective batching":

@@ -10,13 +10,14 @@
  *       section "Continuous batching: reschedule every iteration" — finished
  *         sequences leave and waiting requests are admitted every iteration;
  *         Orca reserves the maximum response length per admitted request;
- *       section "PagedAttention" — the block table lives on the CPU, a block
- *         is allocated only when the previous one fills, blocks are freed when
- *         a request completes, and a request is evicted (and recomputed
- *         later) when HBM is exhausted;
- *       section "Block sharing" — parallel samples share the prompt's blocks,
- *         copy a shared block on the first divergent write, and reference
- *         counts keep a block alive until its last user finishes.
+ *       section "PagedAttention" — the host owns the tables; a sequence
+ *         gets a new block at the moment its last one is full, gives all of
+ *         them back when it ends, and is pushed out (to be recomputed) when
+ *         device memory runs short;
+ *       section "Block sharing" — the samples of one prompt point at the
+ *         prompt's blocks, a shared block is duplicated before a write that
+ *         would make the samples differ, and a per-block count of sharers
+ *         decides when the block is free again.
  *   - "Paging the KV Cache" (lecture 6), section "The waste hiding inside
  *     memory" — a max-length reservation per request fragments memory.
  *   - worksonmygpu.com continuous-batching post, sections "Iteration-level

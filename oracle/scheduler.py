@@ -15,12 +15,14 @@ What the pages fix, and what this module restates:
     length for every admitted request (Module 4, "Continuous batching", the
     tradeoff note; "Paging the KV Cache", section "The waste hiding inside
     memory").
-  * PagedAttention allocates a block only when the previous one fills, frees
-    blocks when a request completes, and evicts a request (discard and
-    recompute later) when HBM runs out (Module 4, section "PagedAttention").
-  * Parallel samples share the prompt's blocks; the first divergent write into
-    a shared block copies it, and reference counts keep a block alive until its
-    last user is done (Module 4, section "Block sharing").
+  * Under PagedAttention a sequence gets a new block at the moment its last
+    one is full, returns all of its blocks when it ends, and is pushed out
+    (dropped, to be recomputed) when device memory runs short (Module 4,
+    section "PagedAttention").
+  * The samples of one prompt point at the prompt's blocks; a shared block is
+    duplicated before a write that would make the samples differ, and a count
+    of sharers per block decides when it is free again (Module 4, section
+    "Block sharing").
   * Prefill and decode share an iteration under a policy that bounds the work
     of one iteration (worksonmygpu.com post, section "The prefill/decode mix").
 

@@ -123,6 +123,20 @@ def _stream(stream) -> int:
     return int(getattr(stream, "cuda_stream", stream))
 
 
+def _expect(t: torch.Tensor, shape: tuple, name: str) -> None:
+    """Host-side shape check: a mismatch would make a kernel read or write past
+    an allocation, so it is refused before anything is launched."""
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _rows(t: torch.Tensor, n: int, name: str) -> int:
+    """A [n][k] int32 table; returns k (0 for an empty table)."""
+    if t.dim() != 2 or t.shape[0] != n:
+        raise ValueError(f"{name} must be [{n}][max_blocks_per_seq], got {tuple(t.shape)}")
+    return int(t.shape[1])
+
+
 def _num_blocks(pool: torch.Tensor, hkv: int, bs: int, d: int) -> int:
     per = 2 * hkv * bs * d
     if pool.numel() % per:
@@ -139,7 +153,11 @@ def _check(fn: str, status: int) -> None:
 
 def pa_append_kv(kv_pool, k_new, v_new, slot_mapping, block_size: int, stream=None) -> None:
     """Write k_new/v_new [T][Hkv][d] into the pool slots ``slot_mapping`` [T] (int32)."""
+    if k_new.dim() != 3:
+        raise ValueError(f"k_new must be [T][Hkv][d], got {tuple(k_new.shape)}")
     T, hkv, d = k_new.shape
+    _expect(v_new, (T, hkv, d), "v_new")
+    _expect(slot_mapping, (T,), "slot_mapping")
     nb = _num_blocks(kv_pool, hkv, block_size, d)
     _check("pa_append_kv", load().pa_append_kv(
         _dev(kv_pool, "kv_pool"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
@@ -152,6 +170,8 @@ def pa_copy_blocks(kv_pool, block_pairs, num_kv_heads: int, head_dim: int, block
     """Copy whole blocks: ``block_pairs`` [P][2] int32 of (src, dst)."""
     nb = _num_blocks(kv_pool, num_kv_heads, block_size, head_dim)
     P = block_pairs.shape[0] if block_pairs.numel() else 0
+    if P:
+        _expect(block_pairs, (P, 2), "block_pairs")
     _check("pa_copy_blocks", load().pa_copy_blocks(
         _dev(kv_pool, "kv_pool"), _i32(block_pairs, "block_pairs") if P else None, P, nb,
         num_kv_heads, head_dim, block_size, _dtype_code(kv_pool), _stream(stream)))
@@ -172,9 +192,13 @@ def new_decode_workspace(num_seqs: int, num_q_heads: int, head_dim: int, max_con
 def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len: int,
               num_kv_heads: int, block_size: int, scale: float, workspace, stream=None):
     """Paged decode attention; fills ``out`` [B][Hq][d] and returns it."""
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B][Hq][d], got {tuple(q.shape)}")
     B, hq, d = q.shape
+    _expect(out, (B, hq, d), "out")
+    _expect(context_lens, (B,), "context_lens")
+    mb = _rows(block_tables, B, "block_tables")
     nb = _num_blocks(kv_pool, num_kv_heads, block_size, d)
-    mb = block_tables.shape[1] if block_tables.dim() == 2 else 0
     _check("pa_decode", load().pa_decode(
         _dev(out, "out"), _dev(q, "q"), _dev(kv_pool, "kv_pool"),
         _i32(block_tables, "block_tables"), _i32(context_lens, "context_lens"), B, mb,
@@ -188,10 +212,16 @@ def pa_prefill_chunk(out, q, kv_pool, block_tables, context_lens, query_start_lo
                      max_chunk_len: int, num_kv_heads: int, block_size: int, scale: float,
                      stream=None):
     """Chunked-prefill attention; fills ``out`` [sum L][Hq][d] and returns it."""
+    if q.dim() != 3:
+        raise ValueError(f"q must be [T][Hq][d], got {tuple(q.shape)}")
     T, hq, d = q.shape
+    _expect(out, (T, hq, d), "out")
+    if context_lens.dim() != 1:
+        raise ValueError(f"context_lens must be [C], got {tuple(context_lens.shape)}")
     C = context_lens.shape[0]
+    _expect(query_start_loc, (C + 1,), "query_start_loc")
+    mb = _rows(block_tables, C, "block_tables")
     nb = _num_blocks(kv_pool, num_kv_heads, block_size, d)
-    mb = block_tables.shape[1] if block_tables.dim() == 2 else 0
     _check("pa_prefill_chunk", load().pa_prefill_chunk(
         _dev(out, "out"), _dev(q, "q"), _dev(kv_pool, "kv_pool"),
         _i32(block_tables, "block_tables"), _i32(context_lens, "context_lens"),
@@ -209,13 +239,28 @@ def pa_mixed_attention(dec_out, dec_q, dec_tables, dec_lens, max_context_len: in
 
     Either side may be empty (a batch of zero sequences, or zero chunks).
     """
+    if dec_q.dim() != 3 or pre_q.dim() != 3:
+        raise ValueError("dec_q must be [B][Hq][d] and pre_q [T][Hq][d]")
     B, hq, d = dec_q.shape
     T = pre_q.shape[0]
+    if pre_lens.dim() != 1:
+        raise ValueError(f"pre_lens must be [C], got {tuple(pre_lens.shape)}")
     C = pre_lens.shape[0]
-    nb = _num_blocks(kv_pool, num_kv_heads, block_size, d)
-    dmb = dec_tables.shape[1] if dec_tables.dim() == 2 else 0
-    pmb = pre_tables.shape[1] if pre_tables.dim() == 2 else 0
     dec_ok, pre_ok = B > 0, C > 0 and T > 0
+    if dec_ok:
+        _expect(dec_out, (B, hq, d), "dec_out")
+        _expect(dec_lens, (B,), "dec_lens")
+    if pre_ok:
+        _expect(pre_q, (T, hq, d), "pre_q")
+        _expect(pre_out, (T, hq, d), "pre_out")
+        _expect(query_start_loc, (C + 1,), "query_start_loc")
+    dmb = _rows(dec_tables, B, "dec_tables") if dec_ok else 0
+    pmb = _rows(pre_tables, C, "pre_tables") if pre_ok else 0
+    nb = _num_blocks(kv_pool, num_kv_heads, block_size, d)
+    # every tensor of a side that runs shares the pool's dtype (an empty side is
+    # not looked at)
+    typed = [kv_pool] + ([dec_q, dec_out] if dec_ok else []) + ([pre_q, pre_out] if pre_ok else [])
+    code = _dtype_code(*typed)
     _check("pa_mixed_attention", load().pa_mixed_attention(
         _dev(dec_out, "dec_out") if dec_ok else None, _dev(dec_q, "dec_q") if dec_ok else None,
         _i32(dec_tables, "dec_tables") if dec_ok else None,
@@ -225,7 +270,7 @@ def pa_mixed_attention(dec_out, dec_q, dec_tables, dec_lens, max_context_len: in
         _i32(pre_lens, "pre_lens") if pre_ok else None,
         _i32(query_start_loc, "query_start_loc") if pre_ok else None, C, T, int(max_chunk_len),
         pmb, _dev(kv_pool, "kv_pool"), hq, num_kv_heads, d, block_size, nb, float(scale),
-        _dtype_code(dec_q, kv_pool), _dev(workspace, "workspace"),
+        code, _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 

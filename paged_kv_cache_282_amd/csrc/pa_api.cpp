@@ -8,6 +8,9 @@
 
 #include "pa_launch.h"
 
+static_assert(pa::kPartition == PA_DECODE_PARTITION,
+              "the kernels' split-K partition must be the one the workspace is sized for");
+
 namespace {
 
 bool supported_dims(int32_t head_dim, int32_t block_size) {

@@ -7,9 +7,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
 
-constexpr int kPartition = 1024;   // split-K partition (tokens), see PA_DECODE_PARTITION
+// Split-K partition (tokens). The public header's macro is the one definition:
+// the workspace size, the grid and every kernel use this constant.
+constexpr int kPartition = PA_DECODE_PARTITION;
 constexpr int kWaves = 4;         // waves per workgroup in the attention kernels
 constexpr int kStep = 32;         // tokens per wave step
 

@@ -1,12 +1,14 @@
 """Minimal host-side KV block manager used to build inputs.
 
-Follows the memory-manager behaviour described on "Module 4 · Batching,
-Scheduling, and Paging" (section "PagedAttention": the CPU keeps a per-sequence
-block table, allocates a new block only when the previous one fills and frees
-blocks when a request completes; section "Block sharing": shared prefix blocks,
-copy-on-write on the first divergent write, reference counts) and on "Paging
-the KV Cache" (section "The waste hiding inside memory": a request's cache is a
-list of page pointers; freed pages go to the next request).
+Behaviour taken from "Module 4 · Batching, Scheduling, and Paging", section
+"PagedAttention" (the host owns each sequence's table of physical blocks; a
+sequence gets a fresh block at the moment its current last block is full, and
+all of its blocks return to the free list when it ends), section "Block
+sharing" (samples of one prompt share its physical blocks, a shared block is
+duplicated before the first write that would make the samples differ, and a
+per-block count of sharers decides when a block is free again), and "Paging
+the KV Cache", section "The waste hiding inside memory" (a request's cache is
+a list of pages, and a finished request's pages are reused by later ones).
 
 Physical placement: the free list is a seeded random permutation of the block
 ids, consumed from the front; freed blocks go to the back.

@@ -6,7 +6,7 @@ GQA long-tail decode, shared-prefix parallel sampling, mixed continuous-batching
 iteration). Ragged, long-tailed lengths and shared prompt prefixes stand in for
 the serving traces the pages describe ("Paging the KV Cache", section "The waste
 hiding inside memory"; the continuous-batching post, section "What this is
-worth, measured": output lengths of high variance, up to 1536 tokens).
+worth, measured": output lengths that spread widely, capped at 1536 tokens).
 
 Storage format written here (the library's documented pool layout): the pool is
 ``num_blocks`` blocks; block ``j`` holds ``2 * Hkv * bs * d`` elements, first the

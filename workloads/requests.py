@@ -1,11 +1,11 @@
 """Seeded synthetic request streams for the scheduler and the engine loop.
 
 Input construction only: prompt lengths, per-sample output lengths and arrival
-iterations. The stand-in for the pages' serving workloads is a stream with
-high variance in output length, up to 1536 tokens (worksonmygpu.com
-continuous-batching post, section "What this is worth, measured"), some of
-whose requests ask for parallel samples of one prompt ("Module 4 · Batching,
-Scheduling, and Paging", section "Block sharing").
+iterations. The stand-in for the pages' serving workloads is a stream whose
+output lengths spread widely, capped at 1536 tokens (the benchmark described in
+the worksonmygpu.com continuous-batching post, section "What this is worth,
+measured"), some of whose requests ask for parallel samples of one prompt
+("Module 4 · Batching, Scheduling, and Paging", section "Block sharing").
 """
 from __future__ import annotations
 
