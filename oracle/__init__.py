@@ -21,9 +21,10 @@ attention routine on contiguous inputs, invariants, and the independent
 pure-Python brute force in ``oracle.brute``). No function here is unpinned.
 """
 from .paged_attention import (append, attend, attend_partitioned, check_slots, copy_blocks,
-                              decode, decode_elements, gather, merge_partials, pool_views,
-                              prefill, swap_blocks)
+                              decode, decode_elements, decode_moments, gather, merge_partials,
+                              pool_views, prefill, prefill_moments, softmax_moments,
+                              swap_blocks)
 
 __all__ = ["append", "attend", "attend_partitioned", "check_slots", "copy_blocks", "decode",
-           "decode_elements", "gather", "merge_partials", "pool_views", "prefill",
-           "swap_blocks"]
+           "decode_elements", "decode_moments", "gather", "merge_partials", "pool_views",
+           "prefill", "prefill_moments", "softmax_moments", "swap_blocks"]

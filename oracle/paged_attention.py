@@ -227,3 +227,67 @@ def merge_partials(parts):
     l = sum(p[1] * np.exp(p[0] - M) for p in finite)
     o = sum(p[2] * np.exp(p[0] - M) for p in finite)
     return o / l
+
+
+# -- weight moments: what a rounding of the weights or of a partial can move ------
+
+def softmax_moments(qv, K, V, sigma):
+    """(o, E_w|V|, E_w|V - o|) of one query, all float64 [d].
+
+    w are the softmax weights of ``sigma * K qv`` (the same definition as
+    ``attend``), o = sum_t w_t V_t, and the two moments are the w-weighted
+    means of |V_t| and of |V_t - o| per dimension. They size the error of an
+    implementation that perturbs each weight by a relative amount (rounding
+    the weights, or inexact scores: at most its bound times E_w|V - o|, since
+    the perturbed weights are renormalised) or rounds partial outputs that
+    are themselves convex combinations of V (at most the rounding unit times
+    E_w|V|). An empty context gives three zero vectors.
+    """
+    n, d = V.shape
+    if n == 0:
+        z = np.zeros(d, np.float64)
+        return z, z.copy(), z.copy()
+    s = sigma * (K @ qv)
+    w = np.exp(s - s.max())
+    w = w / w.sum()
+    o = w @ V
+    return o, w @ np.abs(V), w @ np.abs(V - o)
+
+
+def decode_moments(q, pool, block_tables, context_lens, num_kv_heads, block_size, scale, dtype):
+    """``softmax_moments`` of every (sequence, query head) of a decode batch:
+    three float64 arrays [B][Hq][d] (o, E_w|V|, E_w|V - o|)."""
+    q64 = decode_elements(q, dtype)
+    B, Hq, d = q64.shape
+    G = Hq // num_kv_heads
+    sigma = float(np.float32(scale))
+    res = np.zeros((3, B, Hq, d), np.float64)
+    for b in range(B):
+        n = int(context_lens[b])
+        for g in range(num_kv_heads):
+            K, V = gather(pool, dtype, block_tables[b], n, g, num_kv_heads, block_size, d)
+            for h in range(g * G, (g + 1) * G):
+                res[:, b, h] = softmax_moments(q64[b, h], K, V, sigma)
+    return res[0], res[1], res[2]
+
+
+def prefill_moments(q, pool, block_tables, context_lens, query_start_loc, num_kv_heads,
+                    block_size, scale, dtype):
+    """``softmax_moments`` of every (query, head) of a chunked prefill (the
+    causal key ranges of ``prefill``): three float64 arrays [sum L][Hq][d]."""
+    q64 = decode_elements(q, dtype)
+    T, Hq, d = q64.shape
+    G = Hq // num_kv_heads
+    sigma = float(np.float32(scale))
+    res = np.zeros((3, T, Hq, d), np.float64)
+    for c in range(len(context_lens)):
+        lo, hi = int(query_start_loc[c]), int(query_start_loc[c + 1])
+        L, n = hi - lo, int(context_lens[c])
+        for g in range(num_kv_heads):
+            K, V = gather(pool, dtype, block_tables[c], n, g, num_kv_heads, block_size, d)
+            for i in range(L):
+                a = n - L + i
+                for h in range(g * G, (g + 1) * G):
+                    res[:, lo + i, h] = softmax_moments(q64[lo + i, h], K[: a + 1], V[: a + 1],
+                                                        sigma)
+    return res[0], res[1], res[2]

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # name -> (text in oracle/paged_attention.py, replacement)
 MUTATIONS = {
-    "drop_scale": ("s = sigma * (K @ qv)", "s = (K @ qv)"),
+    "drop_scale": ("s = sigma * (K @ qv)\n    m = s.max()", "s = (K @ qv)\n    m = s.max()"),
     "v_slot_slice_swapped": ("v = vview[blk, g, off // 4, :, off % 4]",
                              "v = vview[blk, g, off % 4, :, off // 4]"),
     "k_slice_transposed": ("k = kview[blk, g, :, off, :].reshape(n, head_dim)",
@@ -26,13 +26,18 @@ MUTATIONS = {
     "gqa_strided_heads": ("for h in range(g * G, (g + 1) * G):\n                out[b, h]",
                           "for h in [x for x in range(Hq) if x % num_kv_heads == g]:\n"
                           "                out[b, h]"),
-    "causal_off_by_one": ("a = n - L + i\n", "a = n - L + i - 1\n"),
+    "causal_off_by_one": ("a = n - L + i\n                for h in range(g * G, (g + 1) * G):\n"
+                          "                    out[",
+                          "a = n - L + i - 1\n                for h in range(g * G, (g + 1) * G):\n"
+                          "                    out["),
     "slot_offset_wrong": ("off = t % block_size", "off = (t // block_size) % block_size"),
     "softmax_sign": ("w = np.exp(s - m)\n    return", "w = np.exp(m - s)\n    return"),
     "append_drops_v": ("        vview[blk, :, off // 4, :, off % 4] = v_new[i]\n", "        pass\n"),
     "copy_without_snapshot": ("out[int(dst)] = snap[int(src)]", "out[int(dst)] = out[int(src)]"),
     "merge_without_rescale": ("l = sum(p[1] * np.exp(p[0] - M) for p in finite)",
                               "l = sum(p[1] for p in finite)"),
+    "moments_unnormalised": ("    w = w / w.sum()\n    o = w @ V", "    o = w @ V / w.sum()"),
+    "moments_deviation_signed": ("w @ np.abs(V - o)", "np.abs(w @ (V - o))"),
 }
 
 # name -> (text in oracle/scheduler.py, replacement); caught by test_sched_oracle.py

@@ -437,3 +437,69 @@ def test_decode_of_empty_context_is_zero():
     out = _decode(w, pool=a, lens=np.array([0, 9], np.int32))
     assert np.array_equal(out[0], np.zeros((2, 8)))
     assert not np.isnan(out[1]).any()
+
+
+# -- weight moments (they size the bf16 error bound of the GPU tests) -------------
+
+def test_moments_of_one_key_are_v_and_zero():
+    """softmax_moments: a single key has weight exactly 1, so E|V| = |V0| and
+    E|V - o| = 0 (closed form)."""
+    V = np.array([[-1.5, 0.25, 3.0]])
+    K = np.array([[0.3, -0.2, 0.9]])
+    o, ma, md = oracle.softmax_moments(np.array([1.0, 2.0, -1.0]), K, V, 0.7)
+    assert np.array_equal(o, V[0]) and np.array_equal(ma, np.abs(V[0]))
+    assert np.array_equal(md, np.zeros(3))
+
+
+def test_moments_of_uniform_weights_are_plain_means():
+    """softmax_moments: q = 0 makes every weight 1/n, so the moments are the
+    plain means of |V| and of |V - mean V| (math.fsum, per dimension)."""
+    rng = np.random.default_rng(17)
+    n, d = 13, 5
+    K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    o, ma, md = oracle.softmax_moments(np.zeros(d), K, V, 0.5)
+    for i in range(d):
+        mean = math.fsum(V[:, i]) / n
+        assert math.isclose(o[i], mean, rel_tol=1e-14, abs_tol=1e-15)
+        assert math.isclose(ma[i], math.fsum(abs(x) for x in V[:, i]) / n, rel_tol=1e-14)
+        assert math.isclose(md[i], math.fsum(abs(x - mean) for x in V[:, i]) / n,
+                            rel_tol=1e-12, abs_tol=1e-15)
+
+
+def test_moments_of_two_keys_follow_the_logistic_weight():
+    """softmax_moments: with two keys whose scores differ by D the weights are
+    1/(1 + e^-D) and 1/(1 + e^D) (closed form), so with V = (a, b) in one
+    dimension E|V| = w0|a| + w1|b| and E|V - o| = 2 w0 w1 |a - b|."""
+    a, b, D = 2.0, -3.0, 1.3
+    K = np.array([[D], [0.0]])
+    V = np.array([[a], [b]])
+    o, ma, md = oracle.softmax_moments(np.array([1.0]), K, V, 1.0)
+    w0 = 1.0 / (1.0 + math.exp(-D))
+    w1 = 1.0 - w0
+    assert math.isclose(o[0], w0 * a + w1 * b, rel_tol=1e-14)
+    assert math.isclose(ma[0], w0 * abs(a) + w1 * abs(b), rel_tol=1e-14)
+    assert math.isclose(md[0], 2 * w0 * w1 * abs(a - b), rel_tol=1e-13)
+
+
+def test_decode_and_prefill_moments_carry_the_oracle_outputs():
+    """decode_moments / prefill_moments gather exactly like decode / prefill:
+    their o equals the oracle's outputs (up to summation order), and the
+    moments satisfy
+    |o| <= E|V| and E|V - o| <= E|V| + |o| (triangle inequality)."""
+    w = make_workload("mixed", num_decode=3, dec_min=1, dec_max=200, num_chunks=2, chunk_len=20,
+                      max_prior=60, num_q_heads=4, num_kv_heads=2, head_dim=16, dtype="f32")
+    p = oracle.append(w.pool, w.k_new, w.v_new, w.slot_mapping, w.num_kv_heads, w.block_size,
+                      w.head_dim)
+    o, ma, md = oracle.decode_moments(w.q, p, w.block_tables, w.context_lens, w.num_kv_heads,
+                                      w.block_size, w.scale, w.dtype)
+    want = oracle.decode(w.q, p, w.block_tables, w.context_lens, w.num_kv_heads, w.block_size,
+                         w.scale, w.dtype)
+    assert np.allclose(o, want, rtol=1e-13, atol=1e-15)
+    assert (np.abs(o) <= ma + 1e-12).all() and (md <= ma + np.abs(o) + 1e-12).all()
+    o2, ma2, md2 = oracle.prefill_moments(w.prefill_q, p, w.prefill_block_tables,
+                                          w.prefill_context_lens, w.query_start_loc,
+                                          w.num_kv_heads, w.block_size, w.scale, w.dtype)
+    want = oracle.prefill(w.prefill_q, p, w.prefill_block_tables, w.prefill_context_lens,
+                          w.query_start_loc, w.num_kv_heads, w.block_size, w.scale, w.dtype)
+    assert np.allclose(o2, want, rtol=1e-13, atol=1e-15)
+    assert (np.abs(o2) <= ma2 + 1e-12).all() and (md2 <= ma2 + np.abs(o2) + 1e-12).all()
