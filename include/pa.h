@@ -249,6 +249,39 @@ int pa_mixed_attention(void* dec_out, const void* dec_q, const int32_t* dec_bloc
                        int32_t num_blocks, float scale, int32_t dtype, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Bytes of the device array that pa_decode_noalloc uses as its workspace
+ * (one array per device, held until the process ends). */
+#define PA_DECODE_SCRATCH_BYTES (64u << 20)
+
+/*
+ * pa_decode_noalloc — pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, or harnesses that
+ * forbid allocation. Same arguments, semantics, validation and results as
+ * pa_decode (bit-identical outputs), without the workspace arguments: the
+ * split-K partials and the work-queue counters live in a device array of
+ * PA_DECODE_SCRATCH_BYTES owned by the library, whose address is looked up at
+ * the first call on each device. Nothing is allocated or freed by any call.
+ *
+ * Limit: the batch's partials, packed in the call's element type, must fit:
+ *   256 + round256(num_seqs * num_q_heads * P * head_dim * e)
+ *       + round256(num_seqs * num_q_heads * P * 8) <= PA_DECODE_SCRATCH_BYTES,
+ * with P = ceil(max_context_len / PA_DECODE_PARTITION) (at least 1), e = 4
+ * for PA_F32 and 2 for PA_BF16; otherwise PA_ERR_WORKSPACE and nothing is
+ * enqueued. (The 256-sequence, 64-query-head, head_dim 128, 8192-token bf16
+ * batch needs about 34 MB.)
+ *
+ * Every call on one device shares that device's array, and each call leaves
+ * its counters at zero. Calls that may overlap in time on one device (on
+ * different streams, or from different host threads without ordering) race
+ * on the array and give undefined results: order them on one stream, or use
+ * pa_decode with separate workspaces.
+ */
+int pa_decode_noalloc(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                      int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                      int32_t dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* pa_status_string(int status);
 

@@ -17,11 +17,13 @@ import os
 import torch
 
 __all__ = ["PAError", "load", "lib_path", "pa_append_kv", "pa_copy_blocks", "pa_decode",
-           "pa_decode_workspace_size", "pa_prefill_chunk", "pa_mixed_attention",
+           "pa_decode_workspace_size", "pa_decode_noalloc", "pa_prefill_chunk",
+           "pa_mixed_attention",
            "pa_swap_blocks", "SWAP_OUT", "SWAP_IN",
            "pa_status_string", "new_decode_workspace", "DECODE_PARTITION"]
 
 DECODE_PARTITION = 1024  # PA_DECODE_PARTITION in include/pa.h
+DECODE_SCRATCH_BYTES = 64 << 20  # PA_DECODE_SCRATCH_BYTES in include/pa.h
 SWAP_OUT, SWAP_IN = 0, 1  # PA_SWAP_OUT, PA_SWAP_IN
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +68,10 @@ def load() -> ctypes.CDLL:
                               _c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _c_int,
                               _c_ptr, ctypes.c_size_t, _c_ptr]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
+                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                      ctypes.c_float, _c_int, _c_ptr]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_prefill_chunk.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int,
                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_int, ctypes.c_float, _c_int, _c_ptr]
@@ -205,6 +211,25 @@ def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len: int,
         int(max_context_len), hq, num_kv_heads, d, block_size, nb, float(scale),
         _dtype_code(q, kv_pool, out), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def pa_decode_noalloc(out, q, kv_pool, block_tables, context_lens, max_context_len: int,
+                      num_kv_heads: int, block_size: int, scale: float, stream=None):
+    """pa_decode without a workspace: the library's own device array serves as
+    one (PA_DECODE_SCRATCH_BYTES per device). Fills ``out`` and returns it."""
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B][Hq][d], got {tuple(q.shape)}")
+    B, hq, d = q.shape
+    _expect(out, (B, hq, d), "out")
+    _expect(context_lens, (B,), "context_lens")
+    mb = _rows(block_tables, B, "block_tables")
+    nb = _num_blocks(kv_pool, num_kv_heads, block_size, d)
+    _check("pa_decode_noalloc", load().pa_decode_noalloc(
+        _dev(out, "out"), _dev(q, "q"), _dev(kv_pool, "kv_pool"),
+        _i32(block_tables, "block_tables"), _i32(context_lens, "context_lens"), B, mb,
+        int(max_context_len), hq, num_kv_heads, d, block_size, nb, float(scale),
+        _dtype_code(q, kv_pool, out), _stream(stream)))
     return out
 
 

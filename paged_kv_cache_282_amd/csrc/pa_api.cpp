@@ -103,24 +103,38 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
 namespace {
 
 // Host checks of a decode batch with at least one sequence (pool and heads
-// already checked).
-int check_decode(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
-                 const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                 int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
-                 int32_t head_dim, int32_t block_size, int32_t dtype, void* workspace,
-                 size_t workspace_bytes) {
-  if (!out || !q || !kv_pool || !block_tables || !context_lens || !workspace) return PA_ERR_NULL;
-  if (!aligned16(out) || !aligned16(q) || !aligned16(kv_pool) || !aligned16(workspace))
-    return PA_ERR_ALIGN;
+// already checked), apart from its workspace.
+int check_decode_batch(void* out, const void* q, const void* kv_pool,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t dtype) {
+  if (!out || !q || !kv_pool || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(kv_pool)) return PA_ERR_ALIGN;
   if (max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   if (int64_t(max_context_len) > int64_t(max_blocks_per_seq) * block_size) return PA_ERR_SHAPE;
   const int64_t parts = pa::decode_max_parts(max_context_len);
   if (int64_t(num_seqs) * num_kv_heads * parts > (int64_t(1) << 30)) return PA_ERR_SHAPE;
   if (int64_t(num_seqs) * num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;  // merge grid
-  if (workspace_bytes < pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len))
-    return PA_ERR_WORKSPACE;
   const size_t qbytes = size_t(num_seqs) * num_q_heads * head_dim * elem_bytes(dtype);
   if (overlaps(out, qbytes, q, qbytes)) return PA_ERR_ALIAS;
+  return PA_OK;
+}
+
+// The same, with a caller's workspace.
+int check_decode(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                 const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                 int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t block_size, int32_t dtype, void* workspace,
+                 size_t workspace_bytes) {
+  if (!workspace) return PA_ERR_NULL;
+  if (!aligned16(workspace)) return PA_ERR_ALIGN;
+  if (int s = check_decode_batch(out, q, kv_pool, block_tables, context_lens, num_seqs,
+                                 max_blocks_per_seq, max_context_len, num_q_heads, num_kv_heads,
+                                 head_dim, block_size, dtype))
+    return s;
+  if (workspace_bytes < pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len))
+    return PA_ERR_WORKSPACE;
   return PA_OK;
 }
 
@@ -162,6 +176,32 @@ int pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* bloc
                                      max_blocks_per_seq, max_context_len, num_q_heads,
                                      shape(num_blocks, num_kv_heads, head_dim, block_size), scale,
                                      dtype, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int pa_decode_noalloc(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                      int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                      int32_t dtype, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || max_context_len < 0) return PA_ERR_SHAPE;
+  if (int s = check_pool(num_blocks, num_kv_heads, head_dim, block_size, dtype)) return s;
+  if (int s = check_heads(num_q_heads, num_kv_heads)) return s;
+  if (num_seqs == 0) return PA_OK;
+  // the library's array stands in for the workspace: every other check of
+  // pa_decode, then the packed layout against the array's size
+  const size_t need = pa::DecodeWorkspace::layout(num_seqs, num_q_heads, head_dim,
+                                                  pa::decode_max_parts(max_context_len),
+                                                  elem_bytes(dtype))
+                          .total;
+  if (int s = check_decode_batch(out, q, kv_pool, block_tables, context_lens, num_seqs,
+                                 max_blocks_per_seq, max_context_len, num_q_heads, num_kv_heads,
+                                 head_dim, block_size, dtype))
+    return s;
+  if (need > pa::kDecodeScratchBytes) return PA_ERR_WORKSPACE;
+  return status_of(pa::launch_decode_noalloc(
+      out, q, kv_pool, block_tables, context_lens, num_seqs, max_blocks_per_seq, max_context_len,
+      num_q_heads, shape(num_blocks, num_kv_heads, head_dim, block_size), scale, dtype,
+      static_cast<hipStream_t>(stream)));
 }
 
 int pa_prefill_chunk(void* out, const void* q, const void* kv_pool,

@@ -33,6 +33,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 namespace pa {
 namespace {
 
@@ -1830,9 +1832,10 @@ namespace {
 DecodeArgs decode_args(void* out, const void* q, const void* pool, const int32_t* tables,
                        const int32_t* lens, int num_seqs, int max_blocks_per_seq,
                        int max_context_len, int num_q_heads, const PoolShape& ps, float scale,
-                       void* workspace, int32_t*& queue) {
+                       void* workspace, int32_t*& queue, size_t o_elem_bytes = sizeof(float)) {
   const int64_t np_max = decode_max_parts(max_context_len);
-  const DecodeWorkspace wl = DecodeWorkspace::layout(num_seqs, num_q_heads, ps.head_dim, np_max);
+  const DecodeWorkspace wl =
+      DecodeWorkspace::layout(num_seqs, num_q_heads, ps.head_dim, np_max, o_elem_bytes);
   DecodeArgs a;
   a.out = out;
   a.q = q;
@@ -1891,14 +1894,16 @@ hipError_t launch_mixed_bf16(const DecodeArgs& da, const PrefillArgs& pa, int gx
 
 }  // namespace
 
-hipError_t launch_decode(void* out, const void* q, const void* pool, const int32_t* tables,
-                         const int32_t* lens, int num_seqs, int max_blocks_per_seq,
-                         int max_context_len, int num_q_heads, const PoolShape& ps, float scale,
-                         int dtype, void* workspace, hipStream_t st) {
-  if (num_seqs == 0) return hipSuccess;
-  int32_t* queue = nullptr;
-  const DecodeArgs a = decode_args(out, q, pool, tables, lens, num_seqs, max_blocks_per_seq,
-                                   max_context_len, num_q_heads, ps, scale, workspace, queue);
+// The allocation-free decode's workspace: one array per device, of fixed size,
+// in the code object's own device memory. Host code never uses the array's
+// name as an address (on the host it only names the symbol): its device
+// address is looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+
+hipError_t dispatch_decode(const DecodeArgs& a, int32_t* queue, int num_q_heads,
+                           const PoolShape& ps, int dtype, hipStream_t st) {
   const int grid = a.n_items;
   const int G = num_q_heads / ps.num_kv_heads;
   const int D = ps.head_dim, BS = ps.block_size;
@@ -1914,6 +1919,66 @@ hipError_t launch_decode(void* out, const void* q, const void* pool, const int32
     if (D == 128 && BS == 32) return launch_decode_f32<128, 32>(a, G, grid, st);
   }
   return hipErrorInvalidValue;
+}
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up (and its queue
+// counters cleared, on `st`) at the first call on that device; nullptr if the
+// lookup fails.
+void* scratch_on_current_device(hipStream_t st) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    // The counters start at zero with the code object; they are cleared once
+    // more here by a kernel (not a memset), so that a caller capturing this
+    // first call into a graph records an ordinary kernel node.
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, st, static_cast<uint32_t*>(p),
+                       64);
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+hipError_t launch_decode(void* out, const void* q, const void* pool, const int32_t* tables,
+                         const int32_t* lens, int num_seqs, int max_blocks_per_seq,
+                         int max_context_len, int num_q_heads, const PoolShape& ps, float scale,
+                         int dtype, void* workspace, hipStream_t st) {
+  if (num_seqs == 0) return hipSuccess;
+  int32_t* queue = nullptr;
+  const DecodeArgs a = decode_args(out, q, pool, tables, lens, num_seqs, max_blocks_per_seq,
+                                   max_context_len, num_q_heads, ps, scale, workspace, queue);
+  return dispatch_decode(a, queue, num_q_heads, ps, dtype, st);
+}
+
+hipError_t launch_decode_noalloc(void* out, const void* q, const void* pool, const int32_t* tables,
+                                 const int32_t* lens, int num_seqs, int max_blocks_per_seq,
+                                 int max_context_len, int num_q_heads, const PoolShape& ps,
+                                 float scale, int dtype, hipStream_t st) {
+  if (num_seqs == 0) return hipSuccess;
+  void* ws = scratch_on_current_device(st);
+  if (ws == nullptr) return hipErrorInvalidSymbol;
+  int32_t* queue = nullptr;
+  const DecodeArgs a =
+      decode_args(out, q, pool, tables, lens, num_seqs, max_blocks_per_seq, max_context_len,
+                  num_q_heads, ps, scale, ws, queue, dtype == 0 ? sizeof(float) : sizeof(uint16_t));
+  return dispatch_decode(a, queue, num_q_heads, ps, dtype, st);
 }
 
 hipError_t launch_prefill(void* out, const void* q, const void* pool, const int32_t* tables,

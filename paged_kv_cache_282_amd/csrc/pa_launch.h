@@ -32,14 +32,17 @@ struct PoolShape {
 // returns them to zero. Partial results need no initialisation.
 struct DecodeWorkspace {
   size_t queue_off, o_off, ml_off, total;
+  // o_elem_bytes: bytes per partial-output element. pa_decode sizes its
+  // caller's workspace for float (4) whatever the call's type; the
+  // allocation-free entry point packs a bf16 call's partials at 2 bytes each.
   static DecodeWorkspace layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
-                                int64_t max_parts) {
+                                int64_t max_parts, size_t o_elem_bytes = sizeof(float)) {
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
     DecodeWorkspace w;
     w.queue_off = 0;
     w.o_off = 256;
-    // partial outputs are float or bf16 (the call's type); sized for float
-    size_t o_bytes = size_t(num_seqs) * num_q_heads * max_parts * head_dim * sizeof(float);
+    // partial outputs are float or bf16 (the call's type)
+    size_t o_bytes = size_t(num_seqs) * num_q_heads * max_parts * head_dim * o_elem_bytes;
     w.ml_off = w.o_off + up(o_bytes);
     size_t ml_bytes = size_t(num_seqs) * num_q_heads * max_parts * 2 * sizeof(float);
     w.total = w.ml_off + up(ml_bytes);
@@ -69,6 +72,15 @@ hipError_t launch_decode(void* out, const void* q, const void* pool, const int32
                          const int32_t* lens, int num_seqs, int max_blocks_per_seq,
                          int max_context_len, int num_q_heads, const PoolShape& ps, float scale,
                          int dtype, void* workspace, hipStream_t stream);
+
+// pa_decode with the library's own scratch array as the workspace (no
+// allocation). The caller has checked that the packed layout (partials in the
+// call's type) fits kDecodeScratchBytes.
+constexpr size_t kDecodeScratchBytes = PA_DECODE_SCRATCH_BYTES;
+hipError_t launch_decode_noalloc(void* out, const void* q, const void* pool, const int32_t* tables,
+                                 const int32_t* lens, int num_seqs, int max_blocks_per_seq,
+                                 int max_context_len, int num_q_heads, const PoolShape& ps,
+                                 float scale, int dtype, hipStream_t stream);
 
 hipError_t launch_prefill(void* out, const void* q, const void* pool, const int32_t* tables,
                           const int32_t* lens, const int32_t* qsl, int num_chunks,

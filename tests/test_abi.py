@@ -36,7 +36,7 @@ def declared_functions(header=HEADER):
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["pa_append_kv", "pa_copy_blocks", "pa_decode",
-                            "pa_decode_workspace_size", "pa_prefill_chunk",
+                            "pa_decode_workspace_size", "pa_decode_noalloc", "pa_prefill_chunk",
                             "pa_mixed_attention", "pa_swap_blocks", "pa_status_string"])
 
 
@@ -103,6 +103,44 @@ def test_decode_validation(lib):
     assert _decode(lib, q=FAKE) == ALIAS                  # out == q
     assert _decode(lib, out=ctypes.c_void_p(0x10008)) == ALIGN
     assert _decode(lib, ws=ctypes.c_void_p(0x10004)) == ALIGN
+
+
+def _noalloc(lib, **kw):
+    a = dict(out=FAKE, q=FAKE2, pool=FAKE, tables=FAKE, lens=FAKE, B=2, MB=4, maxctx=64,
+             hq=8, hkv=2, d=128, bs=16, nb=10, scale=0.1, dtype=BF16, stream=None)
+    a.update(kw)
+    return lib.pa_decode_noalloc(a["out"], a["q"], a["pool"], a["tables"], a["lens"], a["B"],
+                                 a["MB"], a["maxctx"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                 a["nb"], a["scale"], a["dtype"], a["stream"])
+
+
+def test_noalloc_validation(lib):
+    """Every check of pa_decode except the workspace, then the batch's packed
+    partials against the library's array (no call here reaches the device)."""
+    hdr = open(HEADER).read()
+    m = re.search(r"#define\s+PA_DECODE_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == pa.DECODE_SCRATCH_BYTES
+    assert _noalloc(lib, B=0) == OK
+    assert _noalloc(lib, d=96) == UNSUPPORTED
+    assert _noalloc(lib, out=None) == NULL
+    assert _noalloc(lib, maxctx=65) == SHAPE
+    assert _noalloc(lib, q=FAKE) == ALIAS
+    assert _noalloc(lib, out=ctypes.c_void_p(0x10008)) == ALIGN
+
+    def need(B, hq, d, ctx, e):
+        P = max(1, -(-ctx // pa.DECODE_PARTITION))
+        up = lambda x: (x + 255) // 256 * 256
+        return 256 + up(B * hq * P * d * e) + up(B * hq * P * 8)
+
+    # the headline-sized bf16 batch fits (not called: with these fake pointers
+    # a call that passes validation would launch); twice as many sequences in
+    # float32 do not
+    assert need(256, 64, 128, 8192, 2) <= pa.DECODE_SCRATCH_BYTES
+    assert need(512, 64, 128, 8192, 4) > pa.DECODE_SCRATCH_BYTES
+    assert _noalloc(lib, B=512, MB=512, maxctx=8192, hq=64, hkv=8, dtype=F32) == WORKSPACE
+    # the boundary, in sequences of one 1024-token partition, 8 heads, d 128, bf16
+    B = max(b for b in range(1, 40000) if need(b, 8, 128, 1024, 2) <= pa.DECODE_SCRATCH_BYTES)
+    assert _noalloc(lib, B=B + 1, MB=64, maxctx=1024, hq=8, hkv=8) == WORKSPACE
 
 
 def test_append_and_copy_validation(lib):
