@@ -82,6 +82,18 @@ constexpr int kNontemporal = 2;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum of scores that are never NaN (tokens a row may not see are set to
+// -inf first, and slots outside a context are never scored unmasked). The
+// NaN-propagating maximum lowers to v_maximum3_f32 as it stands; the IEEE
+// maxNum of fmaxf needs a quieting v_max of every operand first.
+__device__ __forceinline__ float smax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+__device__ __forceinline__ float smax8(const float (&x)[8]) {
+  return smax(smax(smax(smax(x[0], x[1]), x[2]), smax(smax(x[3], x[4]), x[5])),
+              smax(x[6], x[7]));
+}
+
 // Max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
 // Maximum over the four 16-lane rows of the wave at each lane position: swap
 // halves, then neighbouring rows, with the cross-lane VALU permutes.
@@ -90,10 +102,10 @@ __device__ __forceinline__ float max_over_groups(float x) {
   // have read element 0)
   const uint32_t u = __float_as_uint(x);
   const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  x = smax(__uint_as_float(h[0]), __uint_as_float(h[1]));
   const uint32_t v = __float_as_uint(x);
   const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+  return smax(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 __device__ __forceinline__ float sum_over_groups(float x) {
   x += __shfl_xor(x, 16);
@@ -163,6 +175,10 @@ __device__ __forceinline__ int clamp_block(int blk, int64_t nb) {
 // How far (in base-2 exponent) the running maximum may pass the reference
 // maximum before the softmax state is rescaled; weights stay below 2^8.
 constexpr float kRescaleSlack = 8.f;
+// The reference maximum of a row that has seen no key yet: finite, so that
+// exp2(s - m) needs no special case before the first key (it is 0 for every
+// masked score), and a state with l = 0 adds nothing wherever states merge.
+constexpr float kNoMax = -0x1.0p100f;
 
 template <int D, int BS, int NT>
 struct Bf16Engine {
@@ -176,7 +192,7 @@ struct Bf16Engine {
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      m[nt] = -__builtin_inff();
+      m[nt] = kNoMax;
       l[nt] = 0.f;
       lim[nt] = -1;
 #pragma unroll
@@ -265,10 +281,19 @@ struct Bf16Engine {
   }
 
   // Second half of a step starting at token t0: masks, online softmax and
-  // p.V for every tile. Tokens >= vend have their V zeroed (they may be NaN);
-  // scores of tokens past a row's limit are -inf.
+  // p.V for every tile. With EDGE, tokens >= vend have their V zeroed (they
+  // may be NaN) and scores of tokens past a row's limit are -inf, where the
+  // step reaches that far; without it the caller guarantees that the whole
+  // step lies before vend and at or before every real row's limit.
+  template <bool EDGE = true>
   __device__ __forceinline__ void finish(f32x4 (&sa)[NT], f32x4 (&sb)[NT], u32x4 (&vv)[VT],
                                          int t0, int vend, int lane, float sl2e) {
+    if constexpr (EDGE) edge_masks(sa, sb, vv, t0, vend, lane);
+    softmax_pv(sa, sb, vv, sl2e);
+  }
+
+  __device__ __forceinline__ void edge_masks(f32x4 (&sa)[NT], f32x4 (&sb)[NT], u32x4 (&vv)[VT],
+                                             int t0, int vend, int lane) {
     const int kg = lane >> 4;
     // element e of this lane's eight tokens: e < 4 -> t0 + 4kg + e (set a),
     // e >= 4 -> t0 + 16 + 4kg + e - 4 (set b)
@@ -284,6 +309,28 @@ struct Bf16Engine {
         for (int j = 0; j < VT; ++j) vv[j][w] &= mask;
       }
     }
+    // Mask the scores of tokens past a row's limit. Only steps that reach
+    // past the limit of some real row need it (one wave-uniform test per
+    // step, for every tile at once); then padding rows (lim < 0) are masked
+    // entirely, otherwise their scores are finite and are never read.
+    bool reach = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) reach = reach || (lim[nt] >= 0 && t0 + 31 > lim[nt]);
+    if (__builtin_amdgcn_ballot_w64(reach) != 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sa[nt][i] = (ta0 + i <= lim[nt]) ? sa[nt][i] : -__builtin_inff();
+          sb[nt][i] = (tb0 + i <= lim[nt]) ? sb[nt][i] : -__builtin_inff();
+        }
+      }
+    }
+  }
+
+  // Online softmax and p.V of every tile, on scores already masked.
+  __device__ __forceinline__ void softmax_pv(f32x4 (&sa)[NT], f32x4 (&sb)[NT], u32x4 (&vv)[VT],
+                                             float sl2e) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       // raw scores q.k; the softmax runs in base 2 on q.k * sl2e
@@ -293,48 +340,35 @@ struct Bf16Engine {
         sc[i] = sa[nt][i];
         sc[4 + i] = sb[nt][i];
       }
-      // Mask the scores of tokens past a row's limit. Only steps that reach
-      // past the limit of some real row need it (wave-uniform test); then
-      // padding rows (lim < 0) are masked entirely, otherwise their scores are
-      // finite and are never read.
-      if (__builtin_amdgcn_ballot_w64(lim[nt] >= 0 && t0 + 31 > lim[nt]) != 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tok = e < 4 ? ta0 + e : tb0 + e - 4;
-          sc[e] = (tok <= lim[nt]) ? sc[e] : -__builtin_inff();
-        }
-      }
-      float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-      mx = max_over_groups(mx);
       // scaling by sl2e > 0 is monotone, so the scaled maximum is mx * sl2e.
       // The reference m only moves when the running maximum passes it by more
       // than kRescaleSlack (base 2): until then the weights exp2(s - m) stay
       // below 2^kRescaleSlack, and the state needs no rescale. Any reference
       // gives the same softmax, since O and l share it.
-      const float mtop = fmaxf(m[nt], mx * sl2e);
-      const float mnew =
-          (m[nt] == -__builtin_inff() || mtop > m[nt] + kRescaleSlack) ? mtop : m[nt];
-      const float muse = (mnew == -__builtin_inff()) ? 0.f : mnew;
-      const float alpha = exp2_fast(m[nt] - muse);
+      const float mx = max_over_groups(smax8(sc));
+      const float mtop = smax(m[nt], mx * sl2e);
+      const bool g = mtop > m[nt] + kRescaleSlack;
+      const float mnew = g ? mtop : m[nt];
       bf16x8 p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = static_cast<__bf16>(exp2_fast(fmaf(sc[e], sl2e, -muse)));
+      for (int e = 0; e < 8; ++e) p[e] = static_cast<__bf16>(exp2_fast(fmaf(sc[e], sl2e, -mnew)));
       // the row sum adds the bf16 weights that p.V uses
       float ps = 0.f;
       ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), kOnes2, ps, false);
       ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), kOnes2, ps, false);
       ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), kOnes2, ps, false);
       ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), kOnes2, ps, false);
-      l[nt] = l[nt] * alpha + ps;
-      // o needs rescaling only where a finite maximum grew (elsewhere alpha is
-      // 1, or o is still zero)
-      const bool grew = m[nt] != -__builtin_inff() && mnew > m[nt];
-      m[nt] = mnew;
-      if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+      // l and o need rescaling only where a maximum that had seen a key grew
+      // (elsewhere alpha is 1, or l and o are still zero): the factor, its
+      // exp2 and the products are computed only then
+      if (__builtin_amdgcn_ballot_w64(g && m[nt] != kNoMax) != 0) {
+        const float alpha = exp2_fast(m[nt] - mnew);
+        l[nt] *= alpha;
 #pragma unroll
         for (int j = 0; j < VT; ++j) o[nt][j] *= alpha;
       }
+      l[nt] += ps;
+      m[nt] = mnew;
 #pragma unroll
       for (int j = 0; j < VT; ++j)
         o[nt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv[j]),
@@ -1246,8 +1280,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
   // of the same two dims, which the stash turns into two whole LDS rows.
   // Returns the element offset inside the step's block (A: tokens 0..15 or,
   // at bs 32, all 32) and whether it comes from block B (bs 16, tokens 16..31).
-  auto piece_src = [&](int pc, bool& from_b) -> int64_t {
-    if (pc < kChunks / 2) {
+  auto piece_src = [&](int u, int pc, bool& from_b) -> int64_t {
+    if (u < kPer / 2) {
       const int sl = pc / kStep, t = pc - sl * kStep;
       from_b = BS == 16 && t >= 16;
       const int slot = BS == 16 ? (t & 15) : t;
@@ -1277,15 +1311,19 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       bool from_b;
-      const int64_t off = piece_src(u * 256 + static_cast<int>(threadIdx.x), from_b);
+      const int64_t off = piece_src(u, u * 256 + static_cast<int>(threadIdx.x), from_b);
       pre[u] = ld16((from_b ? bB : bA) + off);
     }
   };
+  // Pieces u < kPer / 2 of a thread are K pieces and the rest V pieces (the
+  // first kChunks / 2 piece numbers are K's); deciding by u keeps the choice
+  // out of the per-lane code.
+  static_assert(kChunks / 2 == (kPer / 2) * 256, "K pieces are the first half of every thread's");
   auto stash = [&](int buf, const u32x4 (&pre)[kPer]) {  // registers -> LDS buffer
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int pc = u * 256 + static_cast<int>(threadIdx.x);
-      if (pc < kChunks / 2) {
+      if (u < kPer / 2) {
         *reinterpret_cast<u32x4*>(&lk[buf * kK + pc * 8]) = pre[u];
       } else {
         // 4 tokens of dims 2dp and 2dp+1 of set `odd` of slice pair cp, 8
@@ -1303,7 +1341,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
   };
   // One step from LDS: the K operands feed the scores, then the V operands are
   // read into registers the K operands no longer need while the softmax runs.
-  auto step = [&](int buf, int t0) {
+  // EDGE: the step may reach past the end of the keys or past some row's
+  // limit (see Bf16Engine::finish).
+  auto step = [&]<bool EDGE>(int buf, int t0) {
     u32x4 kA[KS], kB[KS];
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
@@ -1316,16 +1356,16 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
 #pragma unroll
     for (int j = 0; j < VT; ++j)
       vv[j] = *reinterpret_cast<const u32x4*>(&lv[buf * kV + (kg * D + 16 * j + r) * 8]);
-    eng.finish(sa, sb, vv, t0, kend_wg, lane, a.sl2e);
+    eng.template finish<EDGE>(sa, sb, vv, t0, kend_wg, lane, a.sl2e);
   };
   // Iteration s: fetch step s+2 into `fetch_into` (free: its step s went to
   // LDS in iteration s-1), compute step s from LDS buffer s&1, store step s+1
   // from `held` into LDS buffer (s+1)&1 (last read in iteration s-1, before
   // its barrier), then one barrier.
-  auto iteration = [&](int s, u32x4 (&fetch_into)[kPer], const u32x4 (&held)[kPer]) {
+  auto iteration = [&]<bool EDGE>(int s, u32x4 (&fetch_into)[kPer], const u32x4 (&held)[kPer]) {
     fetch(s + 2, fetch_into);
     const int t0 = s * kStep;
-    if (s < nsteps && i0 < L && t0 < kend) step(s & 1, t0);  // wave-uniform
+    if (s < nsteps && i0 < L && t0 < kend) step.template operator()<EDGE>(s & 1, t0);
     stash((s + 1) & 1, held);
     __syncthreads();
   };
@@ -1334,9 +1374,21 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
   fetch(1, preB);
   stash(0, preA);
   __syncthreads();
-  for (int s = 0; s < nsteps; s += 2) {
-    iteration(s, preA, preB);
-    iteration(s + 1, preB, preA);
+  // Steps before `inner` lie wholly before the end of the keys and at or
+  // before every row's limit of the workgroup (whose smallest is that of its
+  // first position), so they need no masks: a loop of their own keeps its
+  // body free of the mask branches. The rest (about two steps of a tile) test
+  // for masks as they go. Both loops take steps in pairs, as the register
+  // sets alternate.
+  const int inner = max(0, min(nsteps, (prior + wg_i0 + 1) / kStep)) & ~1;
+  int s = 0;
+  for (; s < inner; s += 2) {
+    iteration.template operator()<false>(s, preA, preB);
+    iteration.template operator()<false>(s + 1, preB, preA);
+  }
+  for (; s < nsteps; s += 2) {
+    iteration.template operator()<true>(s, preA, preB);
+    iteration.template operator()<true>(s + 1, preB, preA);
   }
   uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
