@@ -534,6 +534,55 @@ __device__ __forceinline__ void combine_waves(const MergeSmem<D>& sm, int row, i
   }
 }
 
+// Split-K merge of one output row's four dimensions, one partition at a time
+// in partition order (the log-sum-exp identity):
+//   M' = max(M, M_j),  w = L_j 2^(M_j - M'),  L' = L 2^(M - M') + w,
+//   O' = O 2^(M - M') + o_j w,
+// where o_j = O_j / L_j is partition j's normalised output exactly as stored
+// (rounded to the output type) and the result is O / L. Every path that
+// merges partitions -- the persistent decode, which folds each partition as it
+// finishes, and the merge kernel, which reads them from the workspace -- folds
+// with these operations in this order, so a sequence's bits do not depend on
+// which path ran.
+struct MergeState {
+  float M, L;
+  f32x4 O;
+  __device__ __forceinline__ void reset() {
+    M = -__builtin_inff();
+    L = 0.f;
+    O = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void fold(float Mj, float Lj, f32x4 oj) {
+    const float bm = fmaxf(M, Mj);
+    const float f = exp2_fast(M - bm);  // 0 on the first fold (M = -inf)
+    const float w = Lj * exp2_fast(Mj - bm);
+    L = fmaf(L, f, w);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) O[x] = fmaf(oj[x], w, O[x] * f);
+    M = bm;
+  }
+  __device__ __forceinline__ f32x4 result() const {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    return O * inv;
+  }
+};
+
+// A partial output as the merge reads it back: the stored element type's
+// value (bf16 rounding, nearest even) as float.
+template <typename OutT>
+__device__ __forceinline__ f32x4 as_stored(f32x4 v);
+template <>
+__device__ __forceinline__ f32x4 as_stored<float>(f32x4 v) {
+  return v;
+}
+template <>
+__device__ __forceinline__ f32x4 as_stored<uint16_t>(f32x4 v) {
+  f32x4 r;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) r[x] = __uint_as_float(static_cast<uint32_t>(f32_to_bf16_bits(v[x])) << 16);
+  return r;
+}
+
 // After each wave has written its state: a single-partition sequence stores
 // its normalised output; otherwise this partition publishes (M, L, o) for the
 // merge kernel, where o = O / L is the partition's own normalised output,
@@ -676,23 +725,30 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 // Persistent bf16 decode with a dynamic work queue (batches of up to
 // kMaxScanSeqs sequences).
 //
-// Every workgroup first scans the context lengths into LDS: per sequence the
-// number of full 1024-token partitions and whether a shorter trailing one
-// follows. The work items -- (sequence, kv head, partition) -- are numbered
-// full partitions first, then the trailing partial ones, so the queue ends
-// with the smallest items. Workgroups take items from an atomic counter in the
-// workspace until it runs past the last item; the last workgroup to leave
-// returns the counters to zero for the next call. Nothing waits on another
-// workgroup.
+// The unit of work is a whole (sequence, kv head): one workgroup computes its
+// partitions one after another and folds each partition's partial result
+// into the row's merge state in registers as soon as the partition is done
+// (MergeState: the same operations, in the same order, as the merge kernel
+// applies to partials read back from the workspace), so no partial result
+// goes through memory and no merge launch follows.
+//
+// Every workgroup first scans the context lengths into LDS and ranks the
+// sequences into ordering classes, longest first: more partitions first,
+// then single-partition sequences by length in 128-token classes (sequence
+// order inside a class). Units are numbered in that order, the kv heads of a
+// sequence next to each other, so the queue ends with the shortest units and
+// the last units of every workgroup are short. Workgroups take units from an
+// atomic counter in the workspace until it runs past the last one; the last
+// workgroup to leave returns the counters to zero for the next call. Nothing
+// waits on another workgroup.
 // ---------------------------------------------------------------------------
 constexpr int kMaxScanSeqs = 2048;
+constexpr int kOrderClasses = 16;  // ordering classes of the sequences (see order_class)
 
 struct ScanSmem {
-  int full[kMaxScanSeqs + 1];  // exclusive prefix: full partitions before sequence b
-  int part[kMaxScanSeqs + 1];  // exclusive prefix: trailing partial partitions before b
-  int n[kMaxScanSeqs];         // clamped context length
-  int wsum[kWaves][2];
-  int item;
+  int n[kMaxScanSeqs];      // clamped context length
+  int order[kMaxScanSeqs];  // sequences, in unit order
+  int wsum[kOrderClasses / 4][kWaves][2];  // one scratch row per packed scan
   unsigned long long tokens;  // sum of the clamped context lengths
   int shared;                 // some sequence starts with its predecessor's first block
 };
@@ -706,9 +762,23 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int n) {
   return n > a.mb * BS ? a.mb * BS : n;
 }
 
-// Exclusive block-wide scan (256 threads) of a pair of counts.
-__device__ __forceinline__ void block_scan2(ScanSmem& sc, int x, int y, int& ex, int& ey,
-                                            int& tx, int& ty) {
+// Partitions of a context of n tokens (an empty context is one empty item).
+__device__ __forceinline__ int partitions_of(int n) {
+  return n > 0 ? (n + kPartition - 1) / kPartition : 1;
+}
+
+// Ordering class of a sequence: 8 + (partitions - 1), at most 15, for
+// sequences of several partitions; for single-partition sequences its length
+// in 128-token classes (0 .. 7). Larger classes come first.
+__device__ __forceinline__ int order_class(int n) {
+  const int np = partitions_of(n);
+  return np >= 2 ? min(kOrderClasses - 1, 7 + np) : min(7, n / (kPartition / 8));
+}
+
+// Exclusive block-wide scan (256 threads) of a pair of counts; scratch is one
+// row of ScanSmem::wsum, which no other scan of the same call uses.
+__device__ __forceinline__ void block_scan2(int (&wsum)[kWaves][2], int x, int y, int& ex,
+                                            int& ey, int& tx, int& ty) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int ix = x, iy = y;
 #pragma unroll
@@ -720,8 +790,8 @@ __device__ __forceinline__ void block_scan2(ScanSmem& sc, int x, int y, int& ex,
     }
   }
   if (lane == 63) {
-    sc.wsum[wave][0] = ix;
-    sc.wsum[wave][1] = iy;
+    wsum[wave][0] = ix;
+    wsum[wave][1] = iy;
   }
   __syncthreads();
   int bx = 0, by = 0;
@@ -730,69 +800,38 @@ __device__ __forceinline__ void block_scan2(ScanSmem& sc, int x, int y, int& ex,
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     if (w < wave) {
-      bx += sc.wsum[w][0];
-      by += sc.wsum[w][1];
+      bx += wsum[w][0];
+      by += wsum[w][1];
     }
-    tx += sc.wsum[w][0];
-    ty += sc.wsum[w][1];
+    tx += wsum[w][0];
+    ty += wsum[w][1];
   }
   ex = bx + ix - x;
   ey = by + iy - y;
 }
 
-// Largest b in [0, B) with pre[b] <= j, for pre[0] <= j < pre[B].
-__device__ __forceinline__ int search_prefix(const int* pre, int B, int j) {
-  int lo = 0, hi = B;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (pre[mid] <= j) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
-// One queue item: (sequence b, kv head g, partition p) and its token range.
+// One queue item: partition p of unit (sequence b, kv head g) and its token
+// range; np is the sequence's number of partitions.
 struct QItem {
-  int b, g, p, np, tok0, tok1, nsteps;
+  int unit, b, g, p, np, tok0, tok1;
 };
-
-__device__ __forceinline__ void resolve_item(const ScanSmem& sc, int B, int hkv, int n_full_items,
-                                             int k, QItem& it) {
-  if (k < n_full_items) {
-    const int j = k / hkv;
-    it.g = k - j * hkv;
-    it.b = search_prefix(sc.full, B, j);
-    it.p = j - sc.full[it.b];
-  } else {
-    const int k2 = k - n_full_items;
-    const int j = k2 / hkv;
-    it.g = k2 - j * hkv;
-    it.b = search_prefix(sc.part, B, j);
-    it.p = sc.full[it.b + 1] - sc.full[it.b];
-  }
-  const int n = sc.n[it.b];
-  it.np = (sc.full[it.b + 1] - sc.full[it.b]) + (sc.part[it.b + 1] - sc.part[it.b]);
-  it.tok0 = it.p * kPartition;
-  it.tok1 = min(n, it.tok0 + kPartition);
-  it.nsteps = (it.tok1 - it.tok0 + kStep - 1) / kStep;
-}
 
 // An item is the same for the whole workgroup; say so, so that everything
 // derived from it lives in scalar registers.
 __device__ __forceinline__ void make_uniform(QItem& it) {
+  it.unit = __builtin_amdgcn_readfirstlane(it.unit);
   it.b = __builtin_amdgcn_readfirstlane(it.b);
   it.g = __builtin_amdgcn_readfirstlane(it.g);
   it.p = __builtin_amdgcn_readfirstlane(it.p);
   it.np = __builtin_amdgcn_readfirstlane(it.np);
   it.tok0 = __builtin_amdgcn_readfirstlane(it.tok0);
   it.tok1 = __builtin_amdgcn_readfirstlane(it.tok1);
-  it.nsteps = __builtin_amdgcn_readfirstlane(it.nsteps);
 }
 
-// Items are processed as a pipeline. The queue runs two items ahead: while
-// item i computes, every wave already holds the block ids and query of item
-// i+1, and as soon as a wave finishes its steps of item i it issues the first
-// two steps of item i+1, so the workgroup barrier, merge and publish of item i
-// overlap memory traffic of item i+1.
+// Items are processed as a pipeline. While item i computes, every wave already
+// holds the block ids and query of item i+1, and as soon as a wave finishes
+// its steps of item i it issues the first two steps of item i+1, so the
+// workgroup barrier and the fold of item i overlap memory traffic of item i+1.
 //
 // Every load of the step pipeline is issued unconditionally, in straight-line
 // code: a step past the end of its item (or a prefetch past the end of the
@@ -807,7 +846,7 @@ struct DecodeSmem {
 };
 
 // The queue counters live at the start of the decode workspace: [0] the next
-// decode item, [1] workgroups that have left, [2] the next prefill tile of a
+// decode unit, [1] workgroups that have left, [2] the next prefill tile of a
 // mixed launch. The last workgroup to leave returns them to zero.
 __device__ __forceinline__ void leave_queue(int32_t* __restrict__ queue) {
   if (threadIdx.x == 0) {
@@ -824,23 +863,23 @@ __device__ __forceinline__ void leave_queue(int32_t* __restrict__ queue) {
 // may still be in the 256 MiB last-level cache when it is read again.
 constexpr uint64_t kCachedCallBytes = 256ull << 20;
 
-// Every workgroup scans the context lengths into LDS and takes its first two
-// queue items. Returns whether the call's K/V loads should stay cached: when
-// some sequence's first block is also its predecessor's (parallel samples or
-// a cached prefix: the blocks are read again by the other sequences), or when
-// the call reads little enough for the caches to hold it.
+// Every workgroup scans the context lengths into LDS and ranks the sequences
+// into unit order. Returns whether the call's
+// K/V loads should stay cached: when some sequence's first block is also its
+// predecessor's (parallel samples or a cached prefix: the blocks are read
+// again by the other sequences), or when the call reads little enough for the
+// caches to hold it.
 template <int D, int BS>
 __device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __restrict__ queue,
                                             DecodeSmem<D>& ds) {
   ScanSmem& sc = ds.sc;
-  int(&s_next)[2] = ds.s_next;
   const int B = a.num_seqs;
+  constexpr int kPer = kMaxScanSeqs / 256;
+  const int per = (B + 255) / 256;  // thread t owns sequences t*per .. t*per+per-1
+  int nl[kPer], cls[kPer];
+  int shared = 0;
+  uint64_t tok = 0;
   {
-    constexpr int kPer = kMaxScanSeqs / 256;
-    const int per = (B + 255) / 256;
-    int nl[kPer];
-    int fx = 0, py = 0, shared = 0;
-    uint64_t tok = 0;
     // The first table entries are loaded together with the lengths (never
     // behind them), so the scan waits for one round trip to memory.
     int first[kPer], before[kPer];
@@ -859,68 +898,91 @@ __device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __rest
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
       const int i = threadIdx.x * per + c;
+      cls[c] = -1;
       if (c < per && i < B) {
         nl[c] = clamp_len<BS>(a, nl[c]);
-        fx += nl[c] / kPartition;
-        py += (nl[c] % kPartition != 0 || nl[c] == 0) ? 1 : 0;
+        cls[c] = order_class(nl[c]);
         tok += static_cast<uint64_t>(nl[c]);
         shared |= (nl[c] > 0 && first[c] == before[c] &&
                    static_cast<uint32_t>(first[c]) < static_cast<uint64_t>(a.nb)) ? 1 : 0;
       }
     }
-    if (threadIdx.x == 0) {
-      sc.tokens = 0;
-      sc.shared = 0;
-    }
-    int ex, ey, tx, ty;
-    block_scan2(sc, fx, py, ex, ey, tx, ty);  // (its barrier also orders the clears)
-    if (tok != 0) atomicAdd(&sc.tokens, static_cast<unsigned long long>(tok));
-    if (shared) atomicOr(&sc.shared, 1);
-#pragma unroll
-    for (int c = 0; c < kPer; ++c) {
-      const int i = threadIdx.x * per + c;
-      if (c < per && i < B) {
-        sc.full[i] = ex;
-        sc.part[i] = ey;
-        sc.n[i] = nl[c];
-        ex += nl[c] / kPartition;
-        ey += (nl[c] % kPartition != 0 || nl[c] == 0) ? 1 : 0;
-      }
-    }
-    if (threadIdx.x == 0) {
-      sc.full[B] = tx;
-      sc.part[B] = ty;
-      s_next[0] = atomicAdd(&queue[0], 1);
-      s_next[1] = atomicAdd(&queue[0], 1);
-    }
-    __syncthreads();
   }
+  // Count this thread's sequences per class, two 16-bit counts per word (a
+  // count never exceeds kMaxScanSeqs < 2^16), and scan the counts over the
+  // block: each class's start in the order, and this thread's offset in it.
+  int cnt[kOrderClasses / 2];
+#pragma unroll
+  for (int k = 0; k < kOrderClasses / 2; ++k) cnt[k] = 0;
+#pragma unroll
+  for (int c = 0; c < kPer; ++c)
+    if (cls[c] >= 0) cnt[cls[c] >> 1] += 1 << (16 * (cls[c] & 1));
+  if (threadIdx.x == 0) {
+    sc.tokens = 0;
+    sc.shared = 0;
+  }
+  int ex[kOrderClasses / 2], tot[kOrderClasses / 2];
+#pragma unroll
+  for (int k = 0; k < kOrderClasses / 2; k += 2)  // (the first barrier also orders the clears)
+    block_scan2(sc.wsum[k / 2], cnt[k], cnt[k + 1], ex[k], ex[k + 1], tot[k], tot[k + 1]);
+  if (tok != 0) atomicAdd(&sc.tokens, static_cast<unsigned long long>(tok));
+  if (shared) atomicOr(&sc.shared, 1);
+  // class starts, largest class first
+  int start[kOrderClasses];
+  int run = 0;
+#pragma unroll
+  for (int k = kOrderClasses - 1; k >= 0; --k) {
+    start[k] = run;
+    run += (tot[k >> 1] >> (16 * (k & 1))) & 0xFFFF;
+  }
+#pragma unroll
+  for (int c = 0; c < kPer; ++c) {
+    const int i = threadIdx.x * per + c;
+    if (cls[c] >= 0) {
+      int pos = 0, before_here = 0;
+#pragma unroll
+      for (int k = 0; k < kOrderClasses; ++k)
+        if (k == cls[c]) pos = start[k] + ((ex[k >> 1] >> (16 * (k & 1))) & 0xFFFF);
+#pragma unroll
+      for (int c2 = 0; c2 < kPer; ++c2)
+        before_here += (c2 < c && cls[c2] == cls[c]) ? 1 : 0;
+      sc.order[pos + before_here] = i;
+      sc.n[i] = nl[c];
+    }
+  }
+  __syncthreads();
   const uint64_t bytes = sc.tokens * static_cast<uint64_t>(a.hkv) * 2 * D * 2;
   return __builtin_amdgcn_readfirstlane(sc.shared != 0 || bytes <= kCachedCallBytes) != 0;
 }
 
-// The decode pipeline of one workgroup after the scan: takes items until the
+// The decode pipeline of one workgroup after the scan: takes units until the
 // queue runs past the last one. POL is the cache policy of the K/V loads.
+//
+// Units are dealt, not raced for, at the start: of the `dealt` workgroups
+// that start together, the one of rank r takes units r and dealt + r (it
+// needs two: the one it computes and the next one, planned ahead), so the
+// longest units, which come first, go one to a workgroup; every further unit
+// comes from the queue counter, numbered from 2 * dealt. A workgroup that
+// joins later (rank < 0) takes both of its first units from the counter.
 template <int D, int BS, int POL>
 __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __restrict__ queue,
-                                            DecodeSmem<D>& ds) {
+                                            DecodeSmem<D>& ds, int rank, int dealt) {
   using Eng = Bf16Engine<D, BS, 1>;
   constexpr int KS = Eng::KS;
+  constexpr int C4 = D / 4;
   constexpr int kSteps = kPartition / (kWaves * kStep);  // steps per wave per partition
   static_assert(kSteps % 2 == 0, "steps alternate between two register buffers");
+  static_assert(kMaxGroup * C4 <= kWaves * 64, "one thread per (row, 4 dimensions) of a unit");
   MergeSmem<D>(&sm2)[2] = ds.sm2;
   ScanSmem& sc = ds.sc;
   int(&s_next)[2] = ds.s_next;
-  const int B = a.num_seqs;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, kg = lane >> 4;
   const int G = a.hq / a.hkv;
   const uint16_t* pool = static_cast<const uint16_t*>(a.pool);
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
-
-  const int n_full_items = sc.full[B] * a.hkv;
-  const int total = n_full_items + sc.part[B] * a.hkv;
+  const int total = a.num_seqs * a.hkv;  // units
 
   // Block ids of this wave's steps (0 for steps past the item's end) and the
   // query slices of one item. An item is planned one item ahead; its table
@@ -934,12 +996,19 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
     int ent;  // lane l < 2*kSteps: table entry of step l/2, block A (l even) or B
     int idA[kSteps], idB[kSteps];
   };
-  auto plan_item = [&](int k, Plan& pl) {
-    const bool live = k < total;
-    if (live) {
-      resolve_item(sc, B, a.hkv, n_full_items, k, pl.it);
+  auto plan_item = [&](int unit, int p, Plan& pl) {
+    if (unit < total) {
+      const int j = unit / a.hkv;
+      pl.it.unit = unit;
+      pl.it.g = unit - j * a.hkv;
+      pl.it.b = sc.order[j];
+      const int n = sc.n[pl.it.b];
+      pl.it.np = partitions_of(n);
+      pl.it.p = p;
+      pl.it.tok0 = p * kPartition;
+      pl.it.tok1 = min(n, pl.it.tok0 + kPartition);
     } else {
-      pl.it = QItem{0, 0, 0, 1, 0, 0, 0};
+      pl.it = QItem{unit, 0, 0, 0, 1, 0, 0};
     }
     make_uniform(pl.it);
     const int32_t* trow = a.tables + static_cast<int64_t>(pl.it.b) * a.mb;
@@ -981,33 +1050,60 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
                               live);
   };
 
-  // The wave states of item i are merged and published while item i+1's
-  // steps are in flight (after its third and fourth steps' loads are issued),
-  // so that the merge never stands between a step's arrival and the next
-  // loads.
+  // The wave states of item i are combined and folded while item i+1's steps
+  // are in flight (after its third and fourth steps' loads are issued), so
+  // that this never stands between a step's arrival and the next loads.
+  // Thread c < G*C4 owns output row c / C4, dimensions 4 (c % C4) .. +3, of
+  // every unit: a sequence of one partition stores its normalised output
+  // directly; otherwise each partition's normalised output, rounded to bf16
+  // as a stored partial would be, is folded into the thread's merge state,
+  // and the last partition stores the merged row.
+  MergeState ms;
+  ms.reset();
   auto publish = [&](const MergeSmem<D>& sm, const QItem& it) {
-    const int64_t row0 = static_cast<int64_t>(it.b) * a.hq + it.g * G;
-    finish_partition<D, uint16_t>(sm, G, it.np, it.p,
-                                  static_cast<uint16_t*>(a.out) + row0 * D,
-                                  static_cast<uint16_t*>(a.ws_o) + row0 * a.np_max * D,
-                                  a.ws_ml + row0 * a.np_max * 2);
+    const int c = threadIdx.x;
+    if (c >= G * C4) return;
+    const int row = c / C4, dd = 4 * (c - row * C4);
+    float M, L;
+    f32x4 O;
+    combine_waves<D>(sm, row, dd, M, L, O);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint16_t* orow = static_cast<uint16_t*>(a.out) +
+                     (static_cast<int64_t>(it.b) * a.hq + it.g * G + row) * D + dd;
+    if (it.np == 1) {
+      store4<uint16_t>(orow, O * inv);
+      return;
+    }
+    if (it.p == 0) ms.reset();
+    ms.fold(M, L, as_stored<uint16_t>(O * inv));
+    if (it.p == it.np - 1) store4<uint16_t>(orow, ms.result());
   };
 
-  int cur_k = s_next[0], nxt_k = s_next[1];
+  if (rank < 0) {
+    if (threadIdx.x == 0) {
+      s_next[0] = 2 * dealt + atomicAdd(&queue[0], 1);
+      s_next[1] = 2 * dealt + atomicAdd(&queue[0], 1);
+    }
+    __syncthreads();
+  }
+  int cur_u = rank < 0 ? s_next[0] : rank, ahead_u = rank < 0 ? s_next[1] : dealt + rank;
   __syncthreads();  // both slots read before either is rewritten
   int parity = 0;
   Plan cur, nxt;
   QItem prev;  // the item whose states wait in sm2[parity ^ 1]
   bool have_prev = false;
   bf16x8 qcur[KS], qnxt[KS];
-  plan_item(cur_k, cur);
+  plan_item(cur_u, 0, cur);
   block_ids(cur);
   load_query(cur, qcur);
   issue(cur, 0, kv[0]);
   issue(cur, 1, kv[1]);
-  while (cur_k < total) {
+  while (cur.it.unit < total) {
+    // the next item: the current unit's next partition, else the unit taken
+    // ahead (and then another unit is taken from the queue during this item)
+    const bool new_unit = cur.it.p + 1 >= cur.it.np;
+    plan_item(new_unit ? ahead_u : cur.it.unit, new_unit ? 0 : cur.it.p + 1, nxt);
     int after_id = 0;
-    plan_item(nxt_k, nxt);
     eng.init();
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) eng.qreg[0][s2] = qcur[s2];
@@ -1017,10 +1113,10 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
     for (int s2 = 0; s2 < kSteps; ++s2) {
       const int t0 = cur.it.tok0 + kStep * (wave + kWaves * s2);
       if (t0 < cur.it.tok1) eng.compute(kv[s2 & 1], t0, cur.it.tok1, lane, a.sl2e);
-      if (s2 == kSteps - 2 && threadIdx.x == 0) {
-        // Take the item after next; the id goes to LDS just before the
+      if (s2 == kSteps - 2 && new_unit && threadIdx.x == 0) {
+        // Take the unit after next; the id goes to LDS just before the
         // barrier, when waiting for it no longer holds back any load.
-        after_id = atomicAdd(&queue[0], 1);
+        after_id = 2 * dealt + atomicAdd(&queue[0], 1);
       }
       if (s2 == kSteps - 2) {
         block_ids(nxt);
@@ -1034,9 +1130,9 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
     }
     // -- leave the wave states of the current item ---------------------------------
     // One barrier per item: the wave states and the queue slot alternate
-    // between two LDS copies. Item i's copy is read (published) during item
-    // i+1 and rewritten by item i+2, after item i+1's barrier.
-    if (threadIdx.x == 0) s_next[parity] = after_id;
+    // between two LDS copies. Item i's copy is read (folded) during item i+1
+    // and rewritten by item i+2, after item i+1's barrier.
+    if (threadIdx.x == 0 && new_unit) s_next[parity] = after_id;
     MergeSmem<D>& sm = sm2[parity];
     const float lt = sum_over_groups(eng.l[0]);
     if (r < G) {
@@ -1049,35 +1145,34 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
         *reinterpret_cast<f32x4*>(&sm.o[wave][r][16 * j + 4 * kg]) = eng.o[0][j];
     }
     __syncthreads();
-    const int after_k = s_next[parity];
+    if (new_unit) ahead_u = s_next[parity];
     prev = cur.it;
     have_prev = true;
     parity ^= 1;
     cur = nxt;
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) qcur[s2] = qnxt[s2];
-    cur_k = nxt_k;
-    nxt_k = after_k;
   }
   if (have_prev) publish(sm2[parity ^ 1], prev);
 }
 
 // The whole decode of one workgroup: scan, then the loop under the call's
 // cache policy (the same in every workgroup: it depends only on the inputs).
+// rank, dealt: see decode_loop.
 template <int D, int BS>
 __device__ __forceinline__ void decode_persistent(const DecodeArgs& a, int32_t* __restrict__ queue,
-                                                  DecodeSmem<D>& ds) {
+                                                  DecodeSmem<D>& ds, int rank, int dealt) {
   if (decode_scan<D, BS>(a, queue, ds))
-    decode_loop<D, BS, kCached>(a, queue, ds);
+    decode_loop<D, BS, kCached>(a, queue, ds, rank, dealt);
   else
-    decode_loop<D, BS, kNontemporal>(a, queue, ds);
+    decode_loop<D, BS, kNontemporal>(a, queue, ds, rank, dealt);
 }
 
 template <int D, int BS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
   __shared__ DecodeSmem<D> ds;
-  decode_persistent<D, BS>(a, queue, ds);
+  decode_persistent<D, BS>(a, queue, ds, blockIdx.x, gridDim.x);
   leave_queue(queue);
 }
 
@@ -1133,8 +1228,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   // thread combines four output dimensions of one row. It reads the (M, L)
   // of its row itself (the 32 or 16 threads of a row read the same words), so
   // there is no barrier: the partials are read in batches of kBatch
-  // partitions, all loads of a batch issued together, and folded into a
-  // running (M, L, O) that is rescaled when a batch raises the maximum.
+  // partitions, all loads of a batch issued together, and folded one by one
+  // (MergeState).
   constexpr int C4 = D / 4;
   constexpr int kBatch = 8;
   const int bg = blockIdx.x;
@@ -1153,8 +1248,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   // partition pp of this row: (M, L) at mlr[2 * G * pp], o at orow[pp * G * D]
   const float* mlr = a.ws_ml + row0 * a.np_max * 2 + 2 * row;
   const OutT* orow = static_cast<const OutT*>(a.ws_o) + row0 * a.np_max * D + row * D + 4 * c4;
-  float M = -__builtin_inff(), L = 0.f;
-  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  MergeState st;
+  st.reset();
   for (int p0 = 0; p0 < np; p0 += kBatch) {
     float2 ml[kBatch];
     f32x4 v[kBatch];
@@ -1164,27 +1259,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
       ml[u] = *reinterpret_cast<const float2*>(mlr + 2 * G * pp);
       v[u] = load4<OutT>(orow + static_cast<int64_t>(pp) * G * D);
     }
-    float bm = M;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
-      if (p0 + u < np) bm = fmaxf(bm, ml[u].x);
-    if (bm == -__builtin_inff()) continue;
-    const float f = exp2_fast(M - bm);  // 0 while nothing is accumulated
-    L *= f;
-    O *= f;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      if (p0 + u < np) {
-        const float w = ml[u].y * exp2_fast(ml[u].x - bm);
-        L += w;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) O[x] = fmaf(v[u][x], w, O[x]);
-      }
-    }
-    M = bm;
+      if (p0 + u < np) st.fold(ml[u].x, ml[u].y, v[u]);
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  store4<OutT>(static_cast<OutT*>(a.out) + (row0 + row) * D + 4 * c4, O * inv);
+  store4<OutT>(static_cast<OutT*>(a.out) + (row0 + row) * D + 4 * c4, st.result());
 }
 
 // ---------------------------------------------------------------------------
@@ -1493,7 +1572,7 @@ void prefill_bf16_lpt_kernel(PrefillArgs a, int gx) {
 // other list when its first one runs dry. So while both lists last, a CU
 // holds one workgroup of each kind: the HBM-bound decode steps and the
 // MFMA-bound prefill steps overlap instead of running back to back. The
-// split-K merge of long decode sequences still follows as its own kernel.
+// decode side merges the split-K partitions of long sequences itself.
 // ---------------------------------------------------------------------------
 template <int D>
 union MixedSmem {
@@ -1522,13 +1601,16 @@ template <int D, int BS, int NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mixed_bf16_kernel(DecodeArgs da, PrefillArgs pa, int gx, int32_t* __restrict__ queue) {
   __shared__ MixedSmem<D> u;
-  const bool prefill_first = blockIdx.x < gridDim.x / 2;
+  const int half = gridDim.x / 2;
+  const bool prefill_first = blockIdx.x < half;
   if (prefill_first) {
     if (pa.num_chunks > 0) prefill_from_queue<D, BS, NT>(pa, gx, queue, u.p);
     __syncthreads();  // LDS changes hands
-    if (da.num_seqs > 0) decode_persistent<D, BS>(da, queue, u.d);
+    if (da.num_seqs > 0) decode_persistent<D, BS>(da, queue, u.d, -1, gridDim.x - half);
   } else {
-    if (da.num_seqs > 0) decode_persistent<D, BS>(da, queue, u.d);
+    // the decode-first half starts together: its first units are dealt
+    if (da.num_seqs > 0)
+      decode_persistent<D, BS>(da, queue, u.d, blockIdx.x - half, gridDim.x - half);
     __syncthreads();
     if (pa.num_chunks > 0) prefill_from_queue<D, BS, NT>(pa, gx, queue, u.p);
   }
@@ -1759,16 +1841,17 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int grid, int32_t* queue, hip
     // GQA long-tail batch 244.8 -> 239.5 us, MHA batch 185.6 -> 181.6 us,
     // shared-prefix batch 192.8 -> 184.9 us, engine loop (paged) 1.44 -> 1.49 M
     // tokens/s.
+    // The persistent kernel merges split-K partitions itself.
     static const int cus = compute_units();
     const int w = min(grid, cus > 0 ? cus : 256);
     hipLaunchKernelGGL((decode_bf16_persistent_kernel<D, BS>), dim3(w), dim3(256), 0, st, a,
                        queue);
   } else {
     hipLaunchKernelGGL((decode_bf16_kernel<D, BS>), dim3(grid), dim3(256), 0, st, a);
+    if (a.np_max > 1)
+      hipLaunchKernelGGL((decode_merge_kernel<D, BS, uint16_t>), dim3(a.num_seqs * a.hkv),
+                         dim3(256), 0, st, a);
   }
-  if (a.np_max > 1)
-    hipLaunchKernelGGL((decode_merge_kernel<D, BS, uint16_t>), dim3(a.num_seqs * a.hkv), dim3(256),
-                       0, st, a);
   return hipGetLastError();
 }
 
@@ -1936,11 +2019,9 @@ template <int D, int BS>
 hipError_t launch_mixed_bf16(const DecodeArgs& da, const PrefillArgs& pa, int gx, int32_t* queue,
                              hipStream_t st) {
   static const int resident = resident_workgroups(mixed_bf16_kernel<D, BS, kPrefillNT>);
+  // (the persistent decode inside merges its split-K partitions itself)
   hipLaunchKernelGGL((mixed_bf16_kernel<D, BS, kPrefillNT>), dim3(resident > 0 ? resident : 512),
                      dim3(256), 0, st, da, pa, gx, queue);
-  if (da.num_seqs > 0 && da.np_max > 1)
-    hipLaunchKernelGGL((decode_merge_kernel<D, BS, uint16_t>), dim3(da.num_seqs * da.hkv),
-                       dim3(256), 0, st, da);
   return hipGetLastError();
 }
 
