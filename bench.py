@@ -85,6 +85,10 @@ def parse():
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the per-row measurements")
     ap.add_argument("--repeats", type=int, default=20, help="timed calls per batch, per row")
+    ap.add_argument("--sections", default="prefix,prefix1024,mha,mixed,swap",
+                    help="row groups to measure (comma list of prefix, prefix1024, mha, mixed, "
+                         "swap)")
+    ap.add_argument("--no-engine", action="store_true", help="skip the engine-loop rows")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the headline, copy half of the first layer's pool onto the "
                          "other half with one pa_copy_blocks call (a copy of known size for "
@@ -367,19 +371,27 @@ class Rows:
                         f"suffix U[1,512], 32 q / 8 kv heads, bf16, {P} copy pairs",
                         unique_bytes=unique_bytes)
 
-    def run(self, make_workload):
-        import oracle
-        pa = self.pa
-
+    def run(self, make_workload, sections=("prefix", "prefix1024", "mha", "mixed", "swap")):
         # -- shared-prefix batch: the 1032-token reading (a half-full shared last
         # prefix block, copied on the first divergent write), then the literal
         # 1024-token prefix (whole blocks only: nothing to copy) ------------------
-        self.prefix_rows(make_workload, 1032, "")
-        self.torch.cuda.empty_cache()
-        self.prefix_rows(make_workload, 1024, "_len1024")
-        self.torch.cuda.empty_cache()
+        if "prefix" in sections:
+            self.prefix_rows(make_workload, 1032, "")
+            self.torch.cuda.empty_cache()
+        if "prefix1024" in sections:
+            self.prefix_rows(make_workload, 1024, "_len1024")
+            self.torch.cuda.empty_cache()
+        if "mha" in sections:
+            self.mha_rows(make_workload)
+        if "mixed" in sections:
+            self.mixed_rows(make_workload)
+        if "swap" in sections:
+            self.swap_rows(make_workload)
+        return self.out
 
-        # -- MHA batch ------------------------------------------------------------------------
+    def mha_rows(self, make_workload):
+        import oracle
+        pa = self.pa
         w = make_workload("mha")
         d = self.device(w)
         pa.pa_append_kv(d["pool"], d["k_new"], d["v_new"], d["slots"], w.block_size)
@@ -389,7 +401,11 @@ class Rows:
         del d, w
         self.torch.cuda.empty_cache()
 
-        # -- mixed iteration: append of 8432 tokens, decode, chunked prefill --------------
+    def mixed_rows(self, make_workload):
+        """The mixed iteration: append of 8432 tokens, decode, chunked prefill,
+        and the decode and prefill together in one pa_mixed_attention call."""
+        import oracle
+        pa = self.pa
         w = make_workload("mixed")
         d = self.device(w)
         T = len(w.slot_mapping)
@@ -481,7 +497,10 @@ class Rows:
         del d, w, pq, pout, out2, pout2
         self.torch.cuda.empty_cache()
 
-        # -- swap: 1024 blocks of 64 KiB out to pinned host memory and back ----------------
+    def swap_rows(self, make_workload):
+        """1024 blocks of 64 KiB out to pinned host memory and back."""
+        import oracle
+        pa = self.pa
         w = make_workload("gqa")
         pool = to_dev(w.pool, w.dtype, self.torch)
         E = w.block_elems
@@ -508,7 +527,6 @@ class Rows:
                                       f"all {n} blocks, NumPy block copy, 1 thread"),
                          peak_note="PCIe Gen5 x16 nominal, per direction")
         del pool, host
-        return self.out
 
 
 ENGINE_DESC = ("iteration-level serving loop (no model weights): 1024 requests arriving at "
@@ -816,10 +834,12 @@ def main() -> int:
         torch.cuda.empty_cache()
         log("rows:")
         result["rows"] = Rows(pa, torch, args.repeats, not args.no_cpu_baseline,
-                              measured_peak=copy_peak).run(make_workload)
+                              measured_peak=copy_peak).run(make_workload,
+                                                           args.sections.split(","))
         torch.cuda.empty_cache()
-        log("engine loop:")
-        result["engine"] = engine_rows(pa, torch, not args.no_cpu_baseline)
+        if not args.no_engine:
+            log("engine loop:")
+            result["engine"] = engine_rows(pa, torch, not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
     return 0
 
