@@ -301,14 +301,21 @@ class Rows:
     def reps(self, n: int) -> int:
         return max(self.repeats, n) // n * n  # a whole number of rotations per replay
 
-    def decode_row(self, key, w, d, desc, unique_bytes=None):
+    def decode_row(self, key, w, d, desc, unique_bytes=None, hint=None):
+        """hint: the share_prev array; the row then times pa_decode_shared."""
         pa = self.pa
         n = self.rotate(d, rotations(unique_bytes or kv_bytes(w)))
         outs = [d["out"]] + [self.torch.empty_like(d["out"]) for _ in range(n - 1)]
+        share = None if hint is None else i32(hint, self.torch)
 
         def call(i):
-            pa.pa_decode(outs[i], d["q"], d["pools"][i], d["tables"], d["lens"],
-                         w.max_context_len, w.num_kv_heads, w.block_size, w.scale, d["ws"])
+            if share is None:
+                pa.pa_decode(outs[i], d["q"], d["pools"][i], d["tables"], d["lens"],
+                             w.max_context_len, w.num_kv_heads, w.block_size, w.scale, d["ws"])
+            else:
+                pa.pa_decode_shared(outs[i], d["q"], d["pools"][i], d["tables"], d["lens"],
+                                    share, w.max_context_len, w.num_kv_heads, w.block_size,
+                                    w.scale, d["ws"])
 
         ms = time_calls(self.cycled(call, n), self.torch, self.reps(n))
         ns = min(16, w.num_seqs)
@@ -321,11 +328,23 @@ class Rows:
                           w.num_kv_heads, w.block_size, w.scale, w.dtype)
 
         extra = {}
+        if share is not None:
+            # the same call without the hint, on the same pool: bit-identical
+            plain = self.torch.empty_like(d["out"])
+            call(0)
+            pa.pa_decode(plain, d["q"], d["pools"][0], d["tables"], d["lens"], w.max_context_len,
+                         w.num_kv_heads, w.block_size, w.scale, d["ws"])
+            self.torch.cuda.synchronize()
+            extra["bit_identical_to_pa_decode"] = bool(self.torch.equal(
+                outs[0].view(self.torch.int16), plain.view(self.torch.int16)))
+            extra["hint"] = ("share_prev from the tables: leading table entries each sequence "
+                             "has in common with the one before it")
         if unique_bytes is not None:
             extra["unique_bytes"] = unique_bytes
             extra["achieved_unique"] = round(unique_bytes / (ms[0] * 1e-3) / 1e9, 2)
             extra["frac_unique"] = round(unique_bytes / (ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-        self._record(key, "pa_decode", desc, ms, kv_bytes(w), "GB/s", HBM_PEAK_GBS, "hbm",
+        self._record(key, "pa_decode" if share is None else "pa_decode_shared", desc, ms,
+                     kv_bytes(w), "GB/s", HBM_PEAK_GBS, "hbm",
                      self._oracle(orc, sample_bytes / 1e9, "GB/s",
                                   f"decode of the first {ns} sequences (pool after the step's "
                                   f"copy and append), fp64 NumPy, {self.cores} BLAS threads"),
@@ -366,10 +385,13 @@ class Rows:
         uniq = np.unique(np.concatenate([row[: -(-int(n) // w.block_size)]
                                          for row, n in zip(w.block_tables, w.context_lens)]))
         unique_bytes = float(len(uniq)) * blk_bytes
-        self.decode_row("a3_a7_decode_prefix" + suffix, w, d,
-                        f"shared-prefix decode: 32 prompts x 8 samples, prefix {prefix_len}, "
-                        f"suffix U[1,512], 32 q / 8 kv heads, bf16, {P} copy pairs",
-                        unique_bytes=unique_bytes)
+        desc = (f"shared-prefix decode: 32 prompts x 8 samples, prefix {prefix_len}, "
+                f"suffix U[1,512], 32 q / 8 kv heads, bf16, {P} copy pairs")
+        self.decode_row("a3_a7_decode_prefix" + suffix, w, d, desc, unique_bytes=unique_bytes)
+        from workloads import share_prev_hint
+        self.decode_row("a3_a7_decode_prefix_shared" + suffix, w, d,
+                        desc + "; pa_decode_shared with the sharing hint", unique_bytes=unique_bytes,
+                        hint=share_prev_hint(w.block_tables, w.context_lens, w.block_size))
 
     def run(self, make_workload, sections=("prefix", "prefix1024", "mha", "mixed", "swap")):
         # -- shared-prefix batch: the 1032-token reading (a half-full shared last

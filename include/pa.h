@@ -169,6 +169,33 @@ int pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* bloc
               int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_shared — pa_decode for a batch whose sequences share leading
+ * blocks, with the caller saying which. ("Module 4", "Block sharing": the
+ * samples of one prompt point at the same physical blocks for the prompt.)
+ *
+ * Same arguments, checks and results as pa_decode (bit-identical outputs),
+ * plus
+ *   share_prev  device int32 [num_seqs], or NULL (then exactly pa_decode):
+ *               share_prev[b] = the number of leading tokens of sequence b
+ *               that sit in the same physical blocks as sequence b-1's
+ *               (0 or negative: none; share_prev[0] is not read).
+ * The hint only decides which sequences are computed together, never what is
+ * computed: consecutive sequences that share whole PA_DECODE_PARTITION-token
+ * partitions (and each have at least one partition of their own after them)
+ * are stacked, up to 16 query rows, into one MFMA tile, so each shared block
+ * is read once per stack instead of once per sequence. Every shared block id
+ * is checked against each stacked sequence's own table before it is used; a
+ * wrong hint only costs speed. bfloat16 batches of at most 2048 sequences
+ * use it; other calls run pa_decode as it is.
+ */
+int pa_decode_shared(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                     const int32_t* context_lens, const int32_t* share_prev, int32_t num_seqs,
+                     int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, float scale, int32_t dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill_chunk — attention of prefill chunks over a paged cache.
  * (worksonmygpu.com continuous-batching post, "The prefill/decode mix":
  * prompt chunks share the iteration with decode steps.)

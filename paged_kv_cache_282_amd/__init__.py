@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = ["PAError", "load", "lib_path", "pa_append_kv", "pa_copy_blocks", "pa_decode",
-           "pa_decode_workspace_size", "pa_decode_noalloc", "pa_prefill_chunk",
+           "pa_decode_workspace_size", "pa_decode_noalloc", "pa_decode_shared", "pa_prefill_chunk",
            "pa_mixed_attention",
            "pa_swap_blocks", "SWAP_OUT", "SWAP_IN",
            "pa_status_string", "new_decode_workspace", "DECODE_PARTITION"]
@@ -72,6 +72,10 @@ def load() -> ctypes.CDLL:
                                       _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                       ctypes.c_float, _c_int, _c_ptr]
     lib.pa_decode_noalloc.restype = ctypes.c_int
+    lib.pa_decode_shared.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int,
+                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     ctypes.c_float, _c_int, _c_ptr, ctypes.c_size_t, _c_ptr]
+    lib.pa_decode_shared.restype = ctypes.c_int
     lib.pa_prefill_chunk.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int,
                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_int, ctypes.c_float, _c_int, _c_ptr]
@@ -208,6 +212,32 @@ def pa_decode(out, q, kv_pool, block_tables, context_lens, max_context_len: int,
     _check("pa_decode", load().pa_decode(
         _dev(out, "out"), _dev(q, "q"), _dev(kv_pool, "kv_pool"),
         _i32(block_tables, "block_tables"), _i32(context_lens, "context_lens"), B, mb,
+        int(max_context_len), hq, num_kv_heads, d, block_size, nb, float(scale),
+        _dtype_code(q, kv_pool, out), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def pa_decode_shared(out, q, kv_pool, block_tables, context_lens, share_prev,
+                     max_context_len: int, num_kv_heads: int, block_size: int, scale: float,
+                     workspace, stream=None):
+    """pa_decode with the caller's sharing hint ``share_prev`` (int32 [B] device
+    tensor, or None): leading tokens of sequence b stored in sequence b-1's
+    blocks. Same results as pa_decode. Fills ``out`` and returns it."""
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B][Hq][d], got {tuple(q.shape)}")
+    B, hq, d = q.shape
+    _expect(out, (B, hq, d), "out")
+    _expect(context_lens, (B,), "context_lens")
+    share = 0
+    if share_prev is not None:
+        _expect(share_prev, (B,), "share_prev")
+        share = _i32(share_prev, "share_prev")
+    mb = _rows(block_tables, B, "block_tables")
+    nb = _num_blocks(kv_pool, num_kv_heads, block_size, d)
+    _check("pa_decode_shared", load().pa_decode_shared(
+        _dev(out, "out"), _dev(q, "q"), _dev(kv_pool, "kv_pool"),
+        _i32(block_tables, "block_tables"), _i32(context_lens, "context_lens"), share, B, mb,
         int(max_context_len), hq, num_kv_heads, d, block_size, nb, float(scale),
         _dtype_code(q, kv_pool, out), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))

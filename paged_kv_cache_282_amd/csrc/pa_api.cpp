@@ -178,6 +178,27 @@ int pa_decode(void* out, const void* q, const void* kv_pool, const int32_t* bloc
                                      dtype, workspace, static_cast<hipStream_t>(stream)));
 }
 
+int pa_decode_shared(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                     const int32_t* context_lens, const int32_t* share_prev, int32_t num_seqs,
+                     int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, float scale, int32_t dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || max_context_len < 0) return PA_ERR_SHAPE;
+  if (int s = check_pool(num_blocks, num_kv_heads, head_dim, block_size, dtype)) return s;
+  if (int s = check_heads(num_q_heads, num_kv_heads)) return s;
+  if (num_seqs == 0) return PA_OK;
+  if (int s = check_decode(out, q, kv_pool, block_tables, context_lens, num_seqs,
+                           max_blocks_per_seq, max_context_len, num_q_heads, num_kv_heads,
+                           head_dim, block_size, dtype, workspace, workspace_bytes))
+    return s;
+  return status_of(pa::launch_decode(out, q, kv_pool, block_tables, context_lens, num_seqs,
+                                     max_blocks_per_seq, max_context_len, num_q_heads,
+                                     shape(num_blocks, num_kv_heads, head_dim, block_size), scale,
+                                     dtype, workspace, static_cast<hipStream_t>(stream),
+                                     share_prev));
+}
+
 int pa_decode_noalloc(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
                       const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                       int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,

@@ -507,16 +507,16 @@ struct F32Engine {
 // ---------------------------------------------------------------------------
 constexpr int kMaxGroup = 8;  // query heads per kv head handled by the decode kernels
 
-template <int D>
+template <int D, int R = kMaxGroup>
 struct MergeSmem {
-  float o[kWaves][kMaxGroup][D];
-  float m[kWaves][kMaxGroup];
-  float l[kWaves][kMaxGroup];
+  float o[kWaves][R][D];
+  float m[kWaves][R];
+  float l[kWaves][R];
 };
 
 // Combines the kWaves states of row `row` at dimensions dd .. dd+3: (M, L, O).
-template <int D>
-__device__ __forceinline__ void combine_waves(const MergeSmem<D>& sm, int row, int dd, float& M,
+template <int D, int R>
+__device__ __forceinline__ void combine_waves(const MergeSmem<D, R>& sm, int row, int dd, float& M,
                                               float& L, f32x4& O) {
   M = -__builtin_inff();
 #pragma unroll
@@ -605,7 +605,7 @@ __device__ __forceinline__ void finish_partition(const MergeSmem<D>& sm, int row
     const int row = c / C4, dd = 4 * (c - row * C4);
     float M, L;
     f32x4 O;
-    combine_waves<D>(sm, row, dd, M, L, O);
+    combine_waves(sm, row, dd, M, L, O);
     const float inv = L > 0.f ? 1.f / L : 0.f;
     if (np == 1) {
       store4<OutT>(out_rows + row * D + dd, O * inv);
@@ -630,6 +630,9 @@ struct DecodeArgs {
   float sl2e;
   void* ws_o;  // partial outputs, elements of the output type
   float* ws_ml;
+  // Caller's sharing hint (nullptr: none): share[b] leading tokens of sequence
+  // b are said to live in the same blocks as sequence b-1's.
+  const int32_t* share;
 };
 
 // Resolves (sequence, kv head, partition) of this workgroup; false if idle.
@@ -747,11 +750,20 @@ constexpr int kOrderClasses = 16;  // ordering classes of the sequences (see ord
 
 struct ScanSmem {
   int n[kMaxScanSeqs];      // clamped context length
-  int order[kMaxScanSeqs];  // sequences, in unit order
-  int wsum[kOrderClasses / 4][kWaves][2];  // one scratch row per packed scan
+  // Units in queue order: the sequence index (bits 0..10). A unit that
+  // stacks the members of a shared prefix (see decode_loop) also holds its
+  // member count - 1 (bits 11..14) and its shared partitions (bits 16..31).
+  int order[kMaxScanSeqs];
+  int wsum[kOrderClasses / 4 + 1][kWaves][2];  // one scratch row per block scan
   unsigned long long tokens;  // sum of the clamped context lengths
   int shared;                 // some sequence starts with its predecessor's first block
+  int units;                  // number of units per kv head
 };
+static_assert(kMaxScanSeqs <= 2048, "a unit entry keeps the sequence index in 11 bits");
+
+// Rows of MFMA columns a unit of stacked members fills: up to 16 / G members
+// of G query heads each.
+constexpr int kStackRows = 16;
 
 // A context length as the kernels use it: at least 0, at most max_ctx and at
 // most what the table row can address.
@@ -773,6 +785,26 @@ __device__ __forceinline__ int partitions_of(int n) {
 __device__ __forceinline__ int order_class(int n) {
   const int np = partitions_of(n);
   return np >= 2 ? min(kOrderClasses - 1, 7 + np) : min(7, n / (kPartition / 8));
+}
+
+// Exclusive block-wide maximum (256 threads, -1 before thread 0); scratch is
+// one row of ScanSmem::wsum, which no other scan of the same call uses.
+__device__ __forceinline__ int block_max_excl(int (&wsum)[kWaves][2], int x) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int ix = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(ix, d);
+    if (lane >= d) ix = max(ix, o);
+  }
+  if (lane == 63) wsum[wave][0] = ix;
+  __syncthreads();
+  int b = -1;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+    if (w < wave) b = max(b, wsum[w][0]);
+  const int before = __shfl_up(ix, 1);
+  return max(b, lane > 0 ? before : -1);
 }
 
 // Exclusive block-wide scan (256 threads) of a pair of counts; scratch is one
@@ -814,6 +846,10 @@ __device__ __forceinline__ void block_scan2(int (&wsum)[kWaves][2], int x, int y
 // range; np is the sequence's number of partitions.
 struct QItem {
   int unit, b, g, p, np, tok0, tok1;
+  // units that stack shared-prefix members only: the first member b0, the
+  // member count, the shared partitions S, this item's member m (own
+  // partitions p >= S), and whether it is a shared partition (all members)
+  int b0, ucnt, S, m, stacked;
 };
 
 // An item is the same for the whole workgroup; say so, so that everything
@@ -827,6 +863,13 @@ __device__ __forceinline__ void make_uniform(QItem& it) {
   it.tok0 = __builtin_amdgcn_readfirstlane(it.tok0);
   it.tok1 = __builtin_amdgcn_readfirstlane(it.tok1);
 }
+__device__ __forceinline__ void make_uniform_stack(QItem& it) {
+  it.b0 = __builtin_amdgcn_readfirstlane(it.b0);
+  it.ucnt = __builtin_amdgcn_readfirstlane(it.ucnt);
+  it.S = __builtin_amdgcn_readfirstlane(it.S);
+  it.m = __builtin_amdgcn_readfirstlane(it.m);
+  it.stacked = __builtin_amdgcn_readfirstlane(it.stacked);
+}
 
 // Items are processed as a pipeline. While item i computes, every wave already
 // holds the block ids and query of item i+1, and as soon as a wave finishes
@@ -838,11 +881,12 @@ __device__ __forceinline__ void make_uniform(QItem& it) {
 // queue) reads block 0, which stays cached, and is never computed. Loads
 // inside branches would make the compiler's wait counts conservative (wait for
 // all outstanding loads), which serialises loads and compute.
-template <int D>
+template <int D, int R = kMaxGroup>
 struct DecodeSmem {
-  MergeSmem<D> sm2[2];  // wave states of consecutive items alternate
+  MergeSmem<D, R> sm2[2];  // wave states of consecutive items alternate
   ScanSmem sc;
   int s_next[2];
+  int s_ok[2][kWaves];  // stacked items: every member's blocks match (per wave)
 };
 
 // The queue counters live at the start of the decode workspace: [0] the next
@@ -869,14 +913,23 @@ constexpr uint64_t kCachedCallBytes = 256ull << 20;
 // predecessor's (parallel samples or a cached prefix: the blocks are read
 // again by the other sequences), or when the call reads little enough for the
 // caches to hold it.
-template <int D, int BS>
+//
+// SH (a sharing hint is given): a run of consecutive sequences each of which
+// declares that its first partitions live in its predecessor's blocks is cut
+// into stacks of up to kStackRows / G members. A stack whose members all have
+// at least one partition of their own after S >= 1 shared ones becomes one
+// unit (entered under its first member, with the member count and S); its
+// members enter no unit of their own. The declaration is only used to form
+// stacks: decode_loop checks every shared block id before relying on it.
+template <int D, int BS, bool SH, int R>
 __device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __restrict__ queue,
-                                            DecodeSmem<D>& ds) {
+                                            DecodeSmem<D, R>& ds) {
   ScanSmem& sc = ds.sc;
   const int B = a.num_seqs;
   constexpr int kPer = kMaxScanSeqs / 256;
   const int per = (B + 255) / 256;  // thread t owns sequences t*per .. t*per+per-1
-  int nl[kPer], cls[kPer];
+  int nl[kPer], cls[kPer], val[kPer];
+  int claim[kPer];  // SH: shared partitions declared with the predecessor
   int shared = 0;
   uint64_t tok = 0;
   {
@@ -889,26 +942,89 @@ __device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __rest
       nl[c] = 0;
       first[c] = -1;
       before[c] = -2;
+      claim[c] = 0;
       if (c < per && i < B) {
         nl[c] = a.lens[i];
         first[c] = a.tables[static_cast<int64_t>(i) * a.mb];
         if (i > 0) before[c] = a.tables[static_cast<int64_t>(i - 1) * a.mb];
+        if (SH && i > 0) claim[c] = a.share[i];
       }
     }
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
       const int i = threadIdx.x * per + c;
       cls[c] = -1;
+      val[c] = i;
       if (c < per && i < B) {
         nl[c] = clamp_len<BS>(a, nl[c]);
         cls[c] = order_class(nl[c]);
         tok += static_cast<uint64_t>(nl[c]);
         shared |= (nl[c] > 0 && first[c] == before[c] &&
                    static_cast<uint32_t>(first[c]) < static_cast<uint64_t>(a.nb)) ? 1 : 0;
+        // whole partitions of the declared tokens, leaving this sequence at
+        // least one partition of its own
+        claim[c] = claim[c] > 0 ? min(claim[c] / kPartition, partitions_of(nl[c]) - 1) : 0;
       }
     }
   }
-  // Count this thread's sequences per class, two 16-bit counts per word (a
+  if constexpr (SH) {
+    // The lengths and claims go to LDS (the order array serves as scratch
+    // until the ranking below overwrites it), so that each thread can see
+    // its neighbours'.
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int i = threadIdx.x * per + c;
+      if (c < per && i < B) {
+        sc.n[i] = nl[c];
+        sc.order[i] = claim[c];
+      }
+    }
+    __syncthreads();
+    // A claim also needs the predecessor to have a partition of its own after
+    // the shared ones; a sequence without a valid claim starts a run.
+    auto link = [&](int j) {  // shared partitions of sequence j with j - 1 (0: starts a run)
+      return j > 0 ? max(0, min(sc.order[j], partitions_of(sc.n[j - 1]) - 1)) : 0;
+    };
+    int last_start = -1;
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int i = threadIdx.x * per + c;
+      if (c < per && i < B && link(i) == 0) last_start = i;
+    }
+    int run = block_max_excl(sc.wsum[kOrderClasses / 4], last_start);
+    const int G = a.hq / a.hkv;
+    const int gmax = max(1, kStackRows / G);
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int i = threadIdx.x * per + c;
+      if (!(c < per && i < B)) continue;
+      if (link(i) == 0) run = i;
+      // this sequence's stack: lead .. lead+cnt-1, the run cut every gmax members
+      const int lead = i - (i - run) % gmax;
+      int cnt = 1, S = partitions_of(sc.n[lead]) - 1;
+      int64_t total = sc.n[lead];
+      for (int j = lead + 1; j < min(B, lead + gmax); ++j) {
+        const int lj = link(j);
+        if (lj == 0) break;
+        ++cnt;
+        S = min(S, lj);
+        total += sc.n[j];
+      }
+      if (cnt >= 2 && S >= 1) {
+        S = min(S, 0xFFFF);
+        if (i == lead) {
+          // one unit: the shared partitions once, then every member's own
+          const int64_t work = total - static_cast<int64_t>(cnt - 1) * S * kPartition;
+          cls[c] = order_class(static_cast<int>(min<int64_t>(work, 0x7FFFFFFF)));
+          val[c] = i | ((cnt - 1) << 11) | (S << 16);
+          shared = 1;
+        } else {
+          cls[c] = -1;  // computed inside its stack's unit
+        }
+      }
+    }
+  }
+  // Count this thread's units per class, two 16-bit counts per word (a
   // count never exceeds kMaxScanSeqs < 2^16), and scan the counts over the
   // block: each class's start in the order, and this thread's offset in it.
   int cnt[kOrderClasses / 2];
@@ -935,6 +1051,7 @@ __device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __rest
     start[k] = run;
     run += (tot[k >> 1] >> (16 * (k & 1))) & 0xFFFF;
   }
+  if (threadIdx.x == 0) sc.units = run;
 #pragma unroll
   for (int c = 0; c < kPer; ++c) {
     const int i = threadIdx.x * per + c;
@@ -946,9 +1063,9 @@ __device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __rest
 #pragma unroll
       for (int c2 = 0; c2 < kPer; ++c2)
         before_here += (c2 < c && cls[c2] == cls[c]) ? 1 : 0;
-      sc.order[pos + before_here] = i;
-      sc.n[i] = nl[c];
+      sc.order[pos + before_here] = val[c];
     }
+    if (c < per && i < B) sc.n[i] = nl[c];
   }
   __syncthreads();
   const uint64_t bytes = sc.tokens * static_cast<uint64_t>(a.hkv) * 2 * D * 2;
@@ -964,16 +1081,31 @@ __device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __rest
 // longest units, which come first, go one to a workgroup; every further unit
 // comes from the queue counter, numbered from 2 * dealt. A workgroup that
 // joins later (rank < 0) takes both of its first units from the counter.
-template <int D, int BS, int POL>
+//
+// SH: a unit may stack the members b0 .. b0+ucnt-1 of a shared prefix (see
+// decode_scan). Its first S items are the shared partitions, computed once
+// for every member at once: member k's G query rows fill MFMA columns
+// kG .. kG+G-1, and the K/V come through b0's table. MFMA columns and the
+// softmax of each row are independent, so every row's partial is the one
+// its own sequence would compute. Those partials go to the workspace; then
+// each member's own partitions follow, and a member folds the stored shared
+// partials, in partition order, before its first own one: the same
+// operations in the same order as for an unstacked sequence, so the results
+// are bit-identical. A shared item's block ids are checked against every
+// member's table when it is planned; if any differs, that item and the
+// rest of the unit run unstacked instead (b0's item is the same work).
+template <int D, int BS, int POL, bool SH = false, int R = kMaxGroup>
 __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __restrict__ queue,
-                                            DecodeSmem<D>& ds, int rank, int dealt) {
+                                            DecodeSmem<D, R>& ds, int rank, int dealt) {
   using Eng = Bf16Engine<D, BS, 1>;
   constexpr int KS = Eng::KS;
   constexpr int C4 = D / 4;
   constexpr int kSteps = kPartition / (kWaves * kStep);  // steps per wave per partition
   static_assert(kSteps % 2 == 0, "steps alternate between two register buffers");
   static_assert(kMaxGroup * C4 <= kWaves * 64, "one thread per (row, 4 dimensions) of a unit");
-  MergeSmem<D>(&sm2)[2] = ds.sm2;
+  static_assert(!SH || R >= kStackRows, "stacked units need a wave-state row per MFMA column");
+  static_assert(2 * kSteps == 16, "a member's block ids of one wave fill 16 lanes");
+  MergeSmem<D, R>(&sm2)[2] = ds.sm2;
   ScanSmem& sc = ds.sc;
   int(&s_next)[2] = ds.s_next;
   const int lane = threadIdx.x & 63;
@@ -982,7 +1114,7 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
   const int G = a.hq / a.hkv;
   const uint16_t* pool = static_cast<const uint16_t*>(a.pool);
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  const int total = a.num_seqs * a.hkv;  // units
+  const int total = (SH ? sc.units : a.num_seqs) * a.hkv;  // units
 
   // Block ids of this wave's steps (0 for steps past the item's end) and the
   // query slices of one item. An item is planned one item ahead; its table
@@ -995,35 +1127,76 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
     QItem it;
     int ent;  // lane l < 2*kSteps: table entry of step l/2, block A (l even) or B
     int idA[kSteps], idB[kSteps];
+    // SH, shared items: lane l's entry of member 4k + l/16, for the check
+    int entm[kStackRows / 4];
+    bool ok;  // SH: this wave's block ids are every member's
   };
-  auto plan_item = [&](int unit, int p, Plan& pl) {
+  // rows of MFMA columns an item's results occupy
+  auto rows_of = [&](const QItem& it) { return (SH && it.stacked) ? it.ucnt * G : G; };
+  // m, S: SH only -- the member and, within a unit, its shared partitions
+  // (S < 0: the unit's first item, S from the scan)
+  auto plan_item = [&](int unit, int p, Plan& pl, int m = 0, int S = -1) {
     if (unit < total) {
       const int j = unit / a.hkv;
       pl.it.unit = unit;
       pl.it.g = unit - j * a.hkv;
-      pl.it.b = sc.order[j];
-      const int n = sc.n[pl.it.b];
-      pl.it.np = partitions_of(n);
       pl.it.p = p;
       pl.it.tok0 = p * kPartition;
-      pl.it.tok1 = min(n, pl.it.tok0 + kPartition);
+      if constexpr (SH) {
+        const uint32_t v = static_cast<uint32_t>(sc.order[j]);
+        pl.it.b0 = static_cast<int>(v & 2047u);
+        pl.it.ucnt = static_cast<int>((v >> 11) & 15u) + 1;
+        pl.it.S = S >= 0 ? S : static_cast<int>(v >> 16);
+        pl.it.m = m;
+        pl.it.stacked = p < pl.it.S ? 1 : 0;
+      }
+      if (SH && pl.it.stacked) {
+        pl.it.b = pl.it.b0;
+        pl.it.np = 0;
+        pl.it.tok1 = pl.it.tok0 + kPartition;
+      } else {
+        pl.it.b = SH ? pl.it.b0 + m : sc.order[j];
+        const int n = sc.n[pl.it.b];
+        pl.it.np = partitions_of(n);
+        pl.it.tok1 = min(n, pl.it.tok0 + kPartition);
+      }
     } else {
-      pl.it = QItem{unit, 0, 0, 0, 1, 0, 0};
+      pl.it = QItem{unit, 0, 0, 0, 1, 0, 0, 0, 1, 0, 0, 0};
     }
     make_uniform(pl.it);
+    if constexpr (SH) make_uniform_stack(pl.it);
     const int32_t* trow = a.tables + static_cast<int64_t>(pl.it.b) * a.mb;
     const int l = lane < 2 * kSteps ? lane : 0;
     const int base =
         (pl.it.tok0 + kStep * (wave + kWaves * (l >> 1))) / BS + (BS == 16 ? (l & 1) : 0);
     pl.ent = trow[min(base, a.mb - 1)];
+    if constexpr (SH) {
+      if (pl.it.stacked) {
+        // the same 16 entries of every member (16 lanes per member)
+        const int lm = lane & (2 * kSteps - 1);
+        const int bm =
+            (pl.it.tok0 + kStep * (wave + kWaves * (lm >> 1))) / BS + (BS == 16 ? (lm & 1) : 0);
+#pragma unroll
+        for (int k = 0; k < kStackRows / 4; ++k) {
+          const int mm = min(4 * k + (lane >> 4), pl.it.ucnt - 1);
+          pl.entm[k] = 4 * k < pl.it.ucnt
+                           ? a.tables[static_cast<int64_t>(pl.it.b0 + mm) * a.mb + min(bm, a.mb - 1)]
+                           : 0;
+        }
+      }
+    }
   };
   // Query rows g*G .. g*G+G-1 of an item, loaded right before the item's first
   // KV loads, so that waiting for those covers these. Lanes past the group
   // repeat row G-1: those padding rows are never stored, and they are fully
   // masked wherever a step reaches past the context.
   auto load_query = [&](const Plan& pl, bf16x8 (&qv)[KS]) {
+    // a stacked item's column r is head r % G of member r / G
+    const int rr = min(r, rows_of(pl.it) - 1);
+    const int bq = (SH && pl.it.stacked) ? pl.it.b0 + rr / G : pl.it.b;
+    const int hh = (SH && pl.it.stacked) ? rr % G : rr;
     const uint16_t* qr =
-        q + (static_cast<int64_t>(pl.it.b) * a.hq + pl.it.g * G + min(r, G - 1)) * D + 8 * kg;
+        q + (static_cast<int64_t>(bq) * a.hq + pl.it.g * G + hh) * D + 8 * kg;
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) qv[s2] = __builtin_bit_cast(bf16x8, ld16(qr + 32 * s2));
   };
@@ -1037,6 +1210,36 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
       pl.idA[s2] = valid ? clamp_block(ia, a.nb) : 0;
       pl.idB[s2] = (valid && BS == 16 && t0 + 16 < pl.it.tok1) ? clamp_block(ib, a.nb)
                                                                 : pl.idA[s2];
+    }
+    if constexpr (SH) {
+      bool same = true;
+      if (pl.it.stacked) {
+        const int lead = __shfl(pl.ent, lane & (2 * kSteps - 1));
+#pragma unroll
+        for (int k = 0; k < kStackRows / 4; ++k)
+          if (4 * k < pl.it.ucnt) same = same && pl.entm[k] == lead;
+      }
+      pl.ok = __builtin_amdgcn_ballot_w64(!same) == 0;
+    }
+  };
+  // SH: a shared item whose block ids are not every member's (some wave saw
+  // a difference) becomes b0's own item of the same partition, and the unit's
+  // later items run unstacked: S drops to this partition. Its loads (b0's
+  // blocks) are already the right ones, and its query columns 0 .. G-1 are
+  // b0's heads either way.
+  auto unstack_unless_ok = [&](Plan& pl, const int (&ok)[kWaves]) {
+    if constexpr (SH) {
+      if (pl.it.stacked && !(ok[0] && ok[1] && ok[2] && ok[3])) {
+        static_assert(kWaves == 4, "one flag per wave");
+        pl.it.S = pl.it.p;
+        pl.it.stacked = 0;
+        pl.it.m = 0;
+        const int n = sc.n[pl.it.b0];
+        pl.it.np = partitions_of(n);
+        pl.it.tok1 = min(n, pl.it.tok0 + kPartition);
+        make_uniform(pl.it);
+        make_uniform_stack(pl.it);
+      }
     }
   };
   Eng eng;
@@ -1060,13 +1263,40 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
   // and the last partition stores the merged row.
   MergeState ms;
   ms.reset();
-  auto publish = [&](const MergeSmem<D>& sm, const QItem& it) {
+  // SH: partial p of row (sequence b, query head g*G + h) in the workspace, in
+  // the split-K merge's layout: element offset of o (times D) and of (M, L)
+  // (times 2)
+  auto partial_at = [&](int b, int g, int h, int p) -> int64_t {
+    return (static_cast<int64_t>(b) * a.hq + g * G) * a.np_max + static_cast<int64_t>(p) * G + h;
+  };
+  uint16_t* ws_o = static_cast<uint16_t*>(a.ws_o);
+  auto publish = [&](const MergeSmem<D, R>& sm, const QItem& it) {
     const int c = threadIdx.x;
+    if constexpr (SH) {
+      if (it.stacked) {  // every member's partial of this shared partition
+        const int rows = it.ucnt * G;
+        for (int row = c / C4; row < rows; row += kWaves * 64 / C4) {
+          const int dd = 4 * (c % C4);
+          float M, L;
+          f32x4 O;
+          combine_waves(sm, row, dd, M, L, O);
+          const float inv = L > 0.f ? 1.f / L : 0.f;
+          const int mm = row / G, h = row - mm * G;
+          const int64_t at = partial_at(it.b0 + mm, it.g, h, it.p);
+          store4<uint16_t>(ws_o + at * D + dd, O * inv);
+          if (dd == 0) {
+            a.ws_ml[2 * at] = M;
+            a.ws_ml[2 * at + 1] = L;
+          }
+        }
+        return;
+      }
+    }
     if (c >= G * C4) return;
     const int row = c / C4, dd = 4 * (c - row * C4);
     float M, L;
     f32x4 O;
-    combine_waves<D>(sm, row, dd, M, L, O);
+    combine_waves(sm, row, dd, M, L, O);
     const float inv = L > 0.f ? 1.f / L : 0.f;
     uint16_t* orow = static_cast<uint16_t*>(a.out) +
                      (static_cast<int64_t>(it.b) * a.hq + it.g * G + row) * D + dd;
@@ -1075,6 +1305,17 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
       return;
     }
     if (it.p == 0) ms.reset();
+    if constexpr (SH) {
+      if (it.p == it.S && it.S > 0) {
+        // a stacked member's first own partition: its shared partitions'
+        // partials first, as stored, in partition order
+        ms.reset();
+        for (int p2 = 0; p2 < it.S; ++p2) {
+          const int64_t at = partial_at(it.b, it.g, row, p2);
+          ms.fold(a.ws_ml[2 * at], a.ws_ml[2 * at + 1], load4<uint16_t>(ws_o + at * D + dd));
+        }
+      }
+    }
     ms.fold(M, L, as_stored<uint16_t>(O * inv));
     if (it.p == it.np - 1) store4<uint16_t>(orow, ms.result());
   };
@@ -1095,19 +1336,43 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
   bf16x8 qcur[KS], qnxt[KS];
   plan_item(cur_u, 0, cur);
   block_ids(cur);
+  if constexpr (SH) {  // the first item's check, before anything relies on it
+    if (lane == 0) ds.s_ok[1][wave] = cur.ok ? 1 : 0;
+    __syncthreads();
+    unstack_unless_ok(cur, ds.s_ok[1]);
+  }
   load_query(cur, qcur);
   issue(cur, 0, kv[0]);
   issue(cur, 1, kv[1]);
   while (cur.it.unit < total) {
     // the next item: the current unit's next partition, else the unit taken
-    // ahead (and then another unit is taken from the queue during this item)
-    const bool new_unit = cur.it.p + 1 >= cur.it.np;
-    plan_item(new_unit ? ahead_u : cur.it.unit, new_unit ? 0 : cur.it.p + 1, nxt);
+    // ahead (and then another unit is taken from the queue during this item).
+    // SH: a unit's shared partitions, then each member's own partitions.
+    bool new_unit;
+    if constexpr (SH) {
+      const QItem& c = cur.it;
+      if (c.stacked) {
+        new_unit = false;
+        plan_item(c.unit, c.p + 1 < c.S ? c.p + 1 : c.S, nxt, 0, c.S);
+      } else if (c.p + 1 < c.np) {
+        new_unit = false;
+        plan_item(c.unit, c.p + 1, nxt, c.m, c.S);
+      } else if (c.m + 1 < c.ucnt) {
+        new_unit = false;
+        plan_item(c.unit, c.S, nxt, c.m + 1, c.S);
+      } else {
+        new_unit = true;
+        plan_item(ahead_u, 0, nxt);
+      }
+    } else {
+      new_unit = cur.it.p + 1 >= cur.it.np;
+      plan_item(new_unit ? ahead_u : cur.it.unit, new_unit ? 0 : cur.it.p + 1, nxt);
+    }
     int after_id = 0;
     eng.init();
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) eng.qreg[0][s2] = qcur[s2];
-    if (r < G) eng.lim[0] = cur.it.tok1 - 1;
+    if (r < rows_of(cur.it)) eng.lim[0] = cur.it.tok1 - 1;
     // -- steps of the current item; the next item's first two steps follow ------
 #pragma unroll
     for (int s2 = 0; s2 < kSteps; ++s2) {
@@ -1133,9 +1398,12 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
     // between two LDS copies. Item i's copy is read (folded) during item i+1
     // and rewritten by item i+2, after item i+1's barrier.
     if (threadIdx.x == 0 && new_unit) s_next[parity] = after_id;
-    MergeSmem<D>& sm = sm2[parity];
+    if constexpr (SH) {
+      if (lane == 0) ds.s_ok[parity][wave] = nxt.ok ? 1 : 0;
+    }
+    MergeSmem<D, R>& sm = sm2[parity];
     const float lt = sum_over_groups(eng.l[0]);
-    if (r < G) {
+    if (r < rows_of(cur.it)) {
       if (kg == 0) {
         sm.m[wave][r] = eng.m[0];
         sm.l[wave][r] = lt;
@@ -1146,6 +1414,7 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
     }
     __syncthreads();
     if (new_unit) ahead_u = s_next[parity];
+    unstack_unless_ok(nxt, ds.s_ok[parity]);
     prev = cur.it;
     have_prev = true;
     parity ^= 1;
@@ -1159,13 +1428,13 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
 // The whole decode of one workgroup: scan, then the loop under the call's
 // cache policy (the same in every workgroup: it depends only on the inputs).
 // rank, dealt: see decode_loop.
-template <int D, int BS>
+template <int D, int BS, bool SH = false, int R = kMaxGroup>
 __device__ __forceinline__ void decode_persistent(const DecodeArgs& a, int32_t* __restrict__ queue,
-                                                  DecodeSmem<D>& ds, int rank, int dealt) {
-  if (decode_scan<D, BS>(a, queue, ds))
-    decode_loop<D, BS, kCached>(a, queue, ds, rank, dealt);
+                                                  DecodeSmem<D, R>& ds, int rank, int dealt) {
+  if (decode_scan<D, BS, SH>(a, queue, ds))
+    decode_loop<D, BS, kCached, SH, R>(a, queue, ds, rank, dealt);
   else
-    decode_loop<D, BS, kNontemporal>(a, queue, ds, rank, dealt);
+    decode_loop<D, BS, kNontemporal, SH, R>(a, queue, ds, rank, dealt);
 }
 
 template <int D, int BS>
@@ -1173,6 +1442,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
   __shared__ DecodeSmem<D> ds;
   decode_persistent<D, BS>(a, queue, ds, blockIdx.x, gridDim.x);
+  leave_queue(queue);
+}
+
+// The same with the caller's sharing hint: stacked units, whose wave states
+// take kStackRows rows (more LDS than two workgroups per compute unit leave,
+// so one per unit, as the launch uses anyway).
+template <int D, int BS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_bf16_shared_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
+  __shared__ DecodeSmem<D, kStackRows> ds;
+  decode_persistent<D, BS, true, kStackRows>(a, queue, ds, blockIdx.x, gridDim.x);
   leave_queue(queue);
 }
 
@@ -1844,8 +2124,12 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int grid, int32_t* queue, hip
     // The persistent kernel merges split-K partitions itself.
     static const int cus = compute_units();
     const int w = min(grid, cus > 0 ? cus : 256);
-    hipLaunchKernelGGL((decode_bf16_persistent_kernel<D, BS>), dim3(w), dim3(256), 0, st, a,
-                       queue);
+    if (a.share != nullptr)
+      hipLaunchKernelGGL((decode_bf16_shared_kernel<D, BS>), dim3(w), dim3(256), 0, st, a,
+                         queue);
+    else
+      hipLaunchKernelGGL((decode_bf16_persistent_kernel<D, BS>), dim3(w), dim3(256), 0, st, a,
+                         queue);
   } else {
     hipLaunchKernelGGL((decode_bf16_kernel<D, BS>), dim3(grid), dim3(256), 0, st, a);
     if (a.np_max > 1)
@@ -1990,6 +2274,7 @@ DecodeArgs decode_args(void* out, const void* q, const void* pool, const int32_t
   a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
   queue = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.queue_off);
   a.n_items = static_cast<int>(static_cast<int64_t>(num_seqs) * ps.num_kv_heads * np_max);
+  a.share = nullptr;
   return a;
 }
 
@@ -2092,11 +2377,12 @@ void* scratch_on_current_device(hipStream_t st) {
 hipError_t launch_decode(void* out, const void* q, const void* pool, const int32_t* tables,
                          const int32_t* lens, int num_seqs, int max_blocks_per_seq,
                          int max_context_len, int num_q_heads, const PoolShape& ps, float scale,
-                         int dtype, void* workspace, hipStream_t st) {
+                         int dtype, void* workspace, hipStream_t st, const int32_t* share) {
   if (num_seqs == 0) return hipSuccess;
   int32_t* queue = nullptr;
-  const DecodeArgs a = decode_args(out, q, pool, tables, lens, num_seqs, max_blocks_per_seq,
-                                   max_context_len, num_q_heads, ps, scale, workspace, queue);
+  DecodeArgs a = decode_args(out, q, pool, tables, lens, num_seqs, max_blocks_per_seq,
+                             max_context_len, num_q_heads, ps, scale, workspace, queue);
+  a.share = share;  // (only the bf16 persistent decode reads it)
   return dispatch_decode(a, queue, num_q_heads, ps, dtype, st);
 }
 

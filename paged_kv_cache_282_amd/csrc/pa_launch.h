@@ -68,10 +68,13 @@ hipError_t launch_swap(void* pool, void* host_dev, const int32_t* pairs, int num
                        int64_t num_host_blocks, const PoolShape& ps, int dtype,
                        hipStream_t stream);
 
+// share: nullptr, or the caller's sharing hint of pa_decode_shared (device
+// int32 per sequence).
 hipError_t launch_decode(void* out, const void* q, const void* pool, const int32_t* tables,
                          const int32_t* lens, int num_seqs, int max_blocks_per_seq,
                          int max_context_len, int num_q_heads, const PoolShape& ps, float scale,
-                         int dtype, void* workspace, hipStream_t stream);
+                         int dtype, void* workspace, hipStream_t stream,
+                         const int32_t* share = nullptr);
 
 // pa_decode with the library's own scratch array as the workspace (no
 // allocation). The caller has checked that the packed layout (partials in the

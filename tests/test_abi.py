@@ -36,8 +36,9 @@ def declared_functions(header=HEADER):
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["pa_append_kv", "pa_copy_blocks", "pa_decode",
-                            "pa_decode_workspace_size", "pa_decode_noalloc", "pa_prefill_chunk",
-                            "pa_mixed_attention", "pa_swap_blocks", "pa_status_string"])
+                            "pa_decode_workspace_size", "pa_decode_noalloc", "pa_decode_shared",
+                            "pa_prefill_chunk", "pa_mixed_attention", "pa_swap_blocks",
+                            "pa_status_string"])
 
 
 def test_runtime_header_declares_the_runtime():

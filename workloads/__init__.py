@@ -6,8 +6,9 @@ bench and the oracle's tests alike.
 """
 from .block_manager import BlockManager, PoolExhausted
 from .configs import CONFIG_NAMES, Workload, build_decode_workload, make_workload
+from .hints import share_prev_hint
 from .rng import element_bytes, f32_to_bf16_bits, normal_values
 
 __all__ = ["BlockManager", "PoolExhausted", "CONFIG_NAMES", "Workload",
            "build_decode_workload", "make_workload", "element_bytes",
-           "f32_to_bf16_bits", "normal_values"]
+           "f32_to_bf16_bits", "normal_values", "share_prev_hint"]
