@@ -34,6 +34,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 namespace pa {
 namespace {
@@ -1094,7 +1095,11 @@ __device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __rest
 // are bit-identical. A shared item's block ids are checked against every
 // member's table when it is planned; if any differs, that item and the
 // rest of the unit run unstacked instead (b0's item is the same work).
-template <int D, int BS, int POL, bool SH = false, int R = kMaxGroup>
+//
+// HANDOVER: a wave hands over to the next item as soon as its own steps of the
+// current one are done (below); this needs more registers than two
+// workgroups per compute unit leave, so the mixed launch runs without it.
+template <int D, int BS, int POL, bool SH = false, int R = kMaxGroup, bool HANDOVER = false>
 __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __restrict__ queue,
                                             DecodeSmem<D, R>& ds, int rank, int dealt) {
   using Eng = Bf16Engine<D, BS, 1>;
@@ -1244,13 +1249,14 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
   };
   Eng eng;
   typename Eng::KV kv[2];
+  auto issue_ids = [&](int g, int idA, int idB, bool live, typename Eng::KV& buf) {
+    const int64_t kofs = static_cast<int64_t>(g) * BS * D;
+    const int64_t vofs = static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(g) * D * BS;
+    eng.template load_kv<POL>(buf, pool, a.blk_elems, kofs, vofs, idA, idB, lane, live);
+  };
   auto issue = [&](const Plan& pl, int s2, typename Eng::KV& buf) {
-    const int64_t kofs = static_cast<int64_t>(pl.it.g) * BS * D;
-    const int64_t vofs =
-        static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(pl.it.g) * D * BS;
-    const bool live = pl.it.tok0 + kStep * (wave + kWaves * s2) < pl.it.tok1;
-    eng.template load_kv<POL>(buf, pool, a.blk_elems, kofs, vofs, pl.idA[s2], pl.idB[s2], lane,
-                              live);
+    issue_ids(pl.it.g, pl.idA[s2], pl.idB[s2],
+              pl.it.tok0 + kStep * (wave + kWaves * s2) < pl.it.tok1, buf);
   };
 
   // The wave states of item i are combined and folded while item i+1's steps
@@ -1374,6 +1380,7 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
     for (int s2 = 0; s2 < KS; ++s2) eng.qreg[0][s2] = qcur[s2];
     if (r < rows_of(cur.it)) eng.lim[0] = cur.it.tok1 - 1;
     // -- steps of the current item; the next item's first two steps follow ------
+    if constexpr (!HANDOVER) {
 #pragma unroll
     for (int s2 = 0; s2 < kSteps; ++s2) {
       const int t0 = cur.it.tok0 + kStep * (wave + kWaves * s2);
@@ -1392,6 +1399,64 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
       else
         issue(nxt, s2 + 2 - kSteps, kv[s2 & 1]);
       if (s2 == 1 && have_prev) publish(sm2[parity ^ 1], prev);
+    }
+    } else {
+    // This wave's steps of the item: `live` of them reach into it; they are
+    // taken in pairs (kv[0], kv[1]), lw in all. As soon as the last pair's
+    // buffers free up, the next item's steps 0 and 1 are issued into them, so
+    // a short item hands over to the next one at once instead of first
+    // running out its dead steps. The pairs nest, so every load on a path is
+    // issued unconditionally and the compiler's wait counts stay exact.
+    static_assert(kSteps == 8, "four pairs of steps per wave and item");
+    const int len = cur.it.tok1 - cur.it.tok0;
+    const int live = len > kStep * wave ? (len - kStep * wave + kWaves * kStep - 1) / (kWaves * kStep)
+                                        : 0;
+    const int lw = min(kSteps, (live + 1) & ~1);
+    // The hand-over: take the unit after next (the id goes to LDS just before
+    // the barrier, when waiting for it no longer holds back any load), the
+    // next item's block ids and its query rows (read when it starts, by which
+    // time every load issued before them has been waited for anyway).
+    auto hand_over = [&]() {
+      if (new_unit && threadIdx.x == 0) after_id = 2 * dealt + atomicAdd(&queue[0], 1);
+      block_ids(nxt);
+      load_query(nxt, qnxt);
+    };
+    // step s (static) of the current item into / out of kv[s & 1], then the
+    // load of step s + 2, or of the next item's step s & 1 after the last pair
+    auto step_and_issue = [&](auto sc, bool last) {
+      constexpr int s = decltype(sc)::value;
+      const int t0 = cur.it.tok0 + kStep * (wave + kWaves * s);
+      if (t0 < cur.it.tok1) eng.compute(kv[s & 1], t0, cur.it.tok1, lane, a.sl2e);
+      if ((s & 1) == 0 && last) hand_over();
+      const int idA = last ? nxt.idA[s & 1] : (s + 2 < kSteps ? cur.idA[(s + 2) % kSteps] : 0);
+      const int idB = last ? nxt.idB[s & 1] : (s + 2 < kSteps ? cur.idB[(s + 2) % kSteps] : 0);
+      const int g = last ? nxt.it.g : cur.it.g;
+      const bool lv = last ? nxt.it.tok0 + kStep * (wave + kWaves * (s & 1)) < nxt.it.tok1
+                           : cur.it.tok0 + kStep * (wave + kWaves * (s + 2)) < cur.it.tok1;
+      issue_ids(g, idA, idB, lv, kv[s & 1]);
+    };
+    auto pair = [&](auto pc, bool last) {
+      constexpr int s = decltype(pc)::value;
+      step_and_issue(std::integral_constant<int, s>{}, last);
+      step_and_issue(std::integral_constant<int, s + 1>{}, last);
+      if (s == 0 && have_prev) publish(sm2[parity ^ 1], prev);
+    };
+    if (lw == 0) {  // nothing of this item for this wave
+      hand_over();
+      issue_ids(nxt.it.g, nxt.idA[0], nxt.idB[0], nxt.it.tok0 + kStep * wave < nxt.it.tok1, kv[0]);
+      issue_ids(nxt.it.g, nxt.idA[1], nxt.idB[1],
+                nxt.it.tok0 + kStep * (wave + kWaves) < nxt.it.tok1, kv[1]);
+      if (have_prev) publish(sm2[parity ^ 1], prev);
+    } else {
+      pair(std::integral_constant<int, 0>{}, lw == 2);
+      if (lw > 2) {
+        pair(std::integral_constant<int, 2>{}, lw == 4);
+        if (lw > 4) {
+          pair(std::integral_constant<int, 4>{}, lw == 6);
+          if (lw > 6) pair(std::integral_constant<int, 6>{}, true);
+        }
+      }
+    }
     }
     // -- leave the wave states of the current item ---------------------------------
     // One barrier per item: the wave states and the queue slot alternate
@@ -1428,20 +1493,26 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
 // The whole decode of one workgroup: scan, then the loop under the call's
 // cache policy (the same in every workgroup: it depends only on the inputs).
 // rank, dealt: see decode_loop.
-template <int D, int BS, bool SH = false, int R = kMaxGroup>
+template <int D, int BS, bool SH = false, int R = kMaxGroup, bool HANDOVER = false>
 __device__ __forceinline__ void decode_persistent(const DecodeArgs& a, int32_t* __restrict__ queue,
                                                   DecodeSmem<D, R>& ds, int rank, int dealt) {
+  // The hand-over pays where loads return quickly and items are short
+  // (cached calls: shared prefixes, small batches). A streaming call keeps
+  // every wave's loads back to back instead: there the hand-over's extra
+  // branches make the loads wait more (measured 226 -> 237 us on the GQA
+  // long-tail batch), while it gains 124 -> 106 us on the shared-prefix batch.
   if (decode_scan<D, BS, SH>(a, queue, ds))
-    decode_loop<D, BS, kCached, SH, R>(a, queue, ds, rank, dealt);
+    decode_loop<D, BS, kCached, SH, R, HANDOVER>(a, queue, ds, rank, dealt);
   else
-    decode_loop<D, BS, kNontemporal, SH, R>(a, queue, ds, rank, dealt);
+    decode_loop<D, BS, kNontemporal, SH, R, false>(a, queue, ds, rank, dealt);
 }
 
+// (launched one workgroup per compute unit: see launch_decode_bf16)
 template <int D, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_bf16_persistent_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
   __shared__ DecodeSmem<D> ds;
-  decode_persistent<D, BS>(a, queue, ds, blockIdx.x, gridDim.x);
+  decode_persistent<D, BS, false, kMaxGroup, true>(a, queue, ds, blockIdx.x, gridDim.x);
   leave_queue(queue);
 }
 
@@ -1452,7 +1523,7 @@ template <int D, int BS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_bf16_shared_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
   __shared__ DecodeSmem<D, kStackRows> ds;
-  decode_persistent<D, BS, true, kStackRows>(a, queue, ds, blockIdx.x, gridDim.x);
+  decode_persistent<D, BS, true, kStackRows, true>(a, queue, ds, blockIdx.x, gridDim.x);
   leave_queue(queue);
 }
 
