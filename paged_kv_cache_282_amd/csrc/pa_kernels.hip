@@ -1077,11 +1077,13 @@ __device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __rest
 // queue runs past the last one. POL is the cache policy of the K/V loads.
 //
 // Units are dealt, not raced for, at the start: of the `dealt` workgroups
-// that start together, the one of rank r takes units r and dealt + r (it
+// that start together, the one of rank r takes units r and 2*dealt-1-r (it
 // needs two: the one it computes and the next one, planned ahead), so the
-// longest units, which come first, go one to a workgroup; every further unit
-// comes from the queue counter, numbered from 2 * dealt. A workgroup that
-// joins later (rank < 0) takes both of its first units from the counter.
+// longest units, which come first, go one to a workgroup, and the longest of
+// the second round goes with the shortest of the first (a batch of about
+// two units per workgroup ends up balanced); every further unit comes from
+// the queue counter, numbered from 2 * dealt. A workgroup that joins later
+// (rank < 0) takes both of its first units from the counter.
 //
 // SH: a unit may stack the members b0 .. b0+ucnt-1 of a shared prefix (see
 // decode_scan). Its first S items are the shared partitions, computed once
@@ -1333,7 +1335,8 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
     }
     __syncthreads();
   }
-  int cur_u = rank < 0 ? s_next[0] : rank, ahead_u = rank < 0 ? s_next[1] : dealt + rank;
+  int cur_u = rank < 0 ? s_next[0] : rank;
+  int ahead_u = rank < 0 ? s_next[1] : 2 * dealt - 1 - rank;
   __syncthreads();  // both slots read before either is rewritten
   int parity = 0;
   Plan cur, nxt;
