@@ -82,6 +82,10 @@ def parse():
     ap.add_argument("--workload", default="gqa", choices=sorted(WORKLOAD_DESC))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip every oracle timing (headline and rows)")
+    ap.add_argument("--rows-only", action="store_true",
+                    help="skip the headline: only the rows named by --sections (and the engine "
+                         "loop unless --no-engine), for profiling one workload's kernels alone; "
+                         "the JSON line then carries no headline value")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the per-row measurements")
     ap.add_argument("--repeats", type=int, default=20, help="timed calls per batch, per row")
@@ -693,6 +697,16 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
 
+    if args.rows_only:
+        result = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1,
+                  "rows_only": True, "dtype": "bf16", "data": "synthetic"}
+        result["rows"] = Rows(pa, torch, args.repeats, not args.no_cpu_baseline).run(
+            make_workload, args.sections.split(","))
+        if not args.no_engine:
+            result["engine"] = engine_rows(pa, torch, not args.no_cpu_baseline)
+        print(json.dumps(result), flush=True)
+        return 0
+
     t = time.time()
     w = make_workload(args.workload)
     log(f"workload {args.workload}: B={w.num_seqs} tokens={int(w.context_lens.sum())} "
@@ -823,8 +837,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic["hbm_bytes_per_call"],
-                     "kernel": "pa_decode = decode_bf16_persistent_kernel<128,16> + "
-                               "decode_merge_kernel<128,16,bf16>",
+                     "kernel": "pa_decode = decode_bf16_persistent_kernel<128,16> (one "
+                               "launch: split-K partitions are folded inside it)",
                      "algorithmic_bytes_per_launch": int(kv_bytes_layer),
                      "measured_peak": round(copy_peak, 1),
                      "frac_of_measured_peak": round(achieved / copy_peak, 4),
