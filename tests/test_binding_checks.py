@@ -53,6 +53,18 @@ def test_decode_rejects_mismatched_shapes():
         pa.pa_decode(_t(3, 4, 64), _t(12, 64), POOL, _i(3, 2), _i(3), 20, 2, 16, 0.1, ws)
 
 
+def test_decode_shared_rejects_a_hint_of_the_wrong_shape_or_dtype():
+    q = _t(3, 4, 64)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="share_prev"):
+        pa.pa_decode_shared(_t(3, 4, 64), q, POOL, _i(3, 2), _i(3), _i(2), 20, 2, 16, 0.1, ws)
+    with pytest.raises(TypeError, match="share_prev"):
+        pa.pa_decode_shared(_t(3, 4, 64), q, POOL, _i(3, 2), _i(3),
+                            torch.zeros(3, dtype=torch.int64), 20, 2, 16, 0.1, ws)
+    with pytest.raises(ValueError, match="out"):
+        pa.pa_decode_shared(_t(3, 4, 32), q, POOL, _i(3, 2), _i(3), None, 20, 2, 16, 0.1, ws)
+
+
 def test_prefill_rejects_mismatched_shapes():
     q = _t(10, 4, 64)
     with pytest.raises(ValueError, match="out"):
