@@ -106,6 +106,35 @@ def test_decode_validation(lib):
     assert _decode(lib, ws=ctypes.c_void_p(0x10004)) == ALIGN
 
 
+def _shared(lib, share=FAKE, **kw):
+    args = dict(out=FAKE, q=FAKE2, pool=FAKE, tables=FAKE, lens=FAKE, B=2, MB=4, maxctx=64,
+                hq=8, hkv=2, d=128, bs=16, nb=10, scale=0.1, dtype=BF16, ws=FAKE,
+                wsb=1 << 40, stream=None)
+    args.update(kw)
+    return lib.pa_decode_shared(args["out"], args["q"], args["pool"], args["tables"],
+                                args["lens"], share, args["B"], args["MB"], args["maxctx"],
+                                args["hq"], args["hkv"], args["d"], args["bs"], args["nb"],
+                                args["scale"], args["dtype"], args["ws"], args["wsb"],
+                                args["stream"])
+
+
+def test_decode_shared_validation(lib):
+    """pa_decode_shared runs every check of pa_decode (the hint itself is only
+    read on the device, and may be NULL); no call here reaches the device."""
+    assert _shared(lib, B=0) == OK
+    assert _shared(lib, share=None, B=0) == OK
+    assert _shared(lib, dtype=7) == UNSUPPORTED
+    assert _shared(lib, d=96) == UNSUPPORTED
+    assert _shared(lib, hq=7, hkv=2) == SHAPE
+    assert _shared(lib, B=-1) == SHAPE
+    assert _shared(lib, out=None) == NULL
+    assert _shared(lib, ws=None) == NULL
+    assert _shared(lib, maxctx=65) == SHAPE
+    assert _shared(lib, wsb=16) == WORKSPACE
+    assert _shared(lib, q=FAKE) == ALIAS
+    assert _shared(lib, out=ctypes.c_void_p(0x10008)) == ALIGN
+
+
 def _noalloc(lib, **kw):
     a = dict(out=FAKE, q=FAKE2, pool=FAKE, tables=FAKE, lens=FAKE, B=2, MB=4, maxctx=64,
              hq=8, hkv=2, d=128, bs=16, nb=10, scale=0.1, dtype=BF16, stream=None)
