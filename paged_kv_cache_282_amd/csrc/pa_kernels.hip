@@ -17,12 +17,13 @@
 //     each and merge in LDS. A sequence of several partitions publishes one
 //     partial per partition, and a second kernel merges them (log-sum-exp
 //     identity). The grid size and the loads' cache policy follow the batch.
-//   * bf16: scores and p.V run on v_mfma_f32_16x16x32_bf16. The 16 columns of
-//     each MFMA are the query heads of one GQA group (padded) or, in prefill,
-//     (position, head) rows. The pool keeps K in 8-element slices and V in
-//     4-token slices, so every MFMA operand is one contiguous load and each
-//     lane's eight scores are exactly the eight tokens whose V values the same
-//     lane holds for p.V: probabilities never leave registers. Every load
+//   * bf16 decode: scores and p.V run on v_mfma_f32_16x16x32_bf16, whose 16
+//     columns are the query heads of one GQA group (padded); bf16 prefill runs
+//     on v_mfma_f32_32x32x16_bf16, whose 32 columns are (position, head) rows.
+//     The pool keeps K in 8-element slices and V in 4-token slices, so every
+//     MFMA operand is one contiguous load (decode) or LDS read (prefill), and
+//     each lane's scores are exactly the tokens whose V values the same lane
+//     holds for p.V: probabilities never leave registers. Every load
 //     instruction reads a single block through a uniform base address
 //     (decode: a buffer descriptor of one kv head's K or V tile).
 //   * Tokens outside a context are excluded by selection (-inf scores, zeroed
@@ -156,8 +157,8 @@ __device__ __forceinline__ int clamp_block(int blk, int64_t nb) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA engine: online-softmax attention of NT column tiles of 16 query
-// rows over 32-token steps of one kv head.
+// bf16 decode MFMA engine: online-softmax attention of NT column tiles of 16
+// query rows over 32-token steps of one kv head.
 //
 // A step is 32 tokens: set a = tokens 0..15, set b = tokens 16..31 (two
 // blocks of 16, or the two halves of one block of 32).
@@ -1621,6 +1622,137 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Prefill MFMA engine: online-softmax attention of one tile of 32 query rows
+// over 32-token steps, on v_mfma_f32_32x32x16_bf16. That form runs at the
+// matrix cores' full rate on this target, takes half the instructions of the
+// 16x16 form for the same work (each MFMA instruction also costs the VALU a
+// few issue cycles), and gives each lane 16 scores of one row, so a row's
+// maximum needs a single lane swap.
+//
+// Lane (h = lane/32, j = lane%32); "quad" c of a step = its tokens 4c..4c+3.
+//   score MFMA s (dims 16s .. 16s+15)   S^T[tok][row] = K[tok][:] . Q[row][:]
+//     A (K)   lane gives token j, dims 16s + 8h .. +7 (one 8-element K slice)
+//     B (Q)   lane gives row j at the same dims
+//     C       lane holds row j at token 8p + 4h + i as element 4p + i (p, i < 4),
+//             that is quads h, 2+h, 4+h, 6+h
+//   p.V MFMA (dim block db, half m)     O^T[dim][row] += V^T[dim][tok] . P^T[tok][row]
+//     B (P)   lane gives row j at quads 4m+h and 4m+2+h: elements 8m .. 8m+7 of
+//             its own scores, so probabilities never leave registers
+//     A (V^T) lane gives dim 32db + j at the same eight tokens
+//     C       lane holds O^T[32db + 8p + 4h + i][j] as element 4p + i
+// ---------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int D>
+struct PrefillEngine {
+  static constexpr int KS = D / 16;  // score MFMAs (and K operands) per step
+  static constexpr int DB = D / 32;  // 32-dim blocks of O^T
+  bf16x8 qreg[KS];
+  f32x16 o[DB];
+  float m, l;
+  int lim;  // last token this lane's row may attend to (-1: none)
+
+  __device__ __forceinline__ void init() {
+    m = kNoMax;
+    l = 0.f;
+    lim = -1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qreg[s] = bf16x8{};
+  }
+
+  __device__ __forceinline__ void load_q(const uint16_t* q_row, int h) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qreg[s] = __builtin_bit_cast(bf16x8, ld16(q_row + 16 * s + 8 * h));
+  }
+
+  __device__ __forceinline__ f32x16 scores(const u32x4 (&k)[KS]) const {
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k[s]), qreg[s], sc, 0,
+                                                   0, 0);
+    return sc;
+  }
+
+  // Tokens >= vend get their V zeroed (they may be NaN) and scores of tokens
+  // past the row's limit become -inf, where the step reaches that far.
+  // vv[2 * db + m] is the V^T operand of dim block db, half m.
+  __device__ __forceinline__ void edge_masks(f32x16& sc, u32x4 (&vv)[2 * DB], int t0, int vend,
+                                             int h) const {
+    if (t0 + 32 > vend) {  // wave-uniform
+#pragma unroll
+      for (int mh = 0; mh < 2; ++mh) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // word w holds elements 2w, 2w+1: quad 4mh + h (w < 2) or 4mh + 2 + h
+          const int quad = 4 * mh + h + 2 * (w >> 1);
+          const int n = vend - (t0 + 4 * quad);
+          const int e0 = 2 * (w & 1);
+          const uint32_t mask = (e0 < n ? 0x0000FFFFu : 0u) | (e0 + 1 < n ? 0xFFFF0000u : 0u);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) vv[2 * db + mh][w] &= mask;
+        }
+      }
+    }
+    // Only steps that reach past the limit of some real row need the score
+    // mask; then padding rows (lim < 0) are masked entirely, otherwise their
+    // scores are finite and never read.
+    if (__builtin_amdgcn_ballot_w64(lim >= 0 && t0 + 31 > lim) != 0) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[4 * p + i] = (t0 + 8 * p + 4 * h + i <= lim) ? sc[4 * p + i] : -__builtin_inff();
+    }
+  }
+
+  // Online softmax and p.V on scores already masked (see Bf16Engine for the
+  // rescale slack and the bf16 weight sums).
+  __device__ __forceinline__ void softmax_pv(const f32x16& sc, const u32x4 (&vv)[2 * DB],
+                                             float sl2e) {
+    float mx = sc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = smax(mx, sc[e]);
+    {  // the other half of the row (lane ^ 32)
+      const uint32_t u = __float_as_uint(mx);
+      const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      mx = smax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mtop = smax(m, mx * sl2e);
+    const bool grow = mtop > m + kRescaleSlack;
+    const float mnew = grow ? mtop : m;
+    bf16x8 p[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      p[e >> 3][e & 7] = static_cast<__bf16>(exp2_fast(fmaf(sc[e], sl2e, -mnew)));
+    float ps = 0.f;
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh) {
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[mh], p[mh], 0, 1), kOnes2, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[mh], p[mh], 2, 3), kOnes2, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[mh], p[mh], 4, 5), kOnes2, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[mh], p[mh], 6, 7), kOnes2, ps, false);
+    }
+    if (__builtin_amdgcn_ballot_w64(grow && m != kNoMax) != 0) {
+      const float alpha = exp2_fast(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    l += ps;
+    m = mnew;
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv[2 * db + mh]),
+                                                        p[mh], o[db], 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Chunked prefill.
 // ---------------------------------------------------------------------------
 struct PrefillArgs {
@@ -1647,40 +1779,44 @@ __device__ __forceinline__ bool chunk_geometry(const PrefillArgs& a, int c, int 
   return true;
 }
 
-// bf16: a wave owns NT tiles of 16 rows; row R -> (position R / G, head R % G).
-// The workgroup's four waves cover consecutive positions and share one key
-// range, so each 32-token step of K and V is loaded from HBM once per
-// workgroup (16-byte loads by all 256 threads, issued a step ahead) into one of
-// two LDS buffers, and every wave reads its MFMA operands from there.
+// bf16: a wave owns one tile of kPrefillRows rows; row R -> (position R / G,
+// head R % G). The workgroup's four waves cover consecutive positions and
+// share one key range, so each 32-token step of K and V is loaded from HBM
+// once per workgroup (16-byte loads by all 256 threads, issued a step ahead)
+// into one of two LDS buffers, and every wave reads its MFMA operands from
+// there.
+constexpr int kPrefillRows = 32;
+
 template <int D>
 struct PrefillSmem {
-  uint16_t k[2][(D / 8) * kStep * 8];        // [slice][token][8], tokens of one step
-  // [slice pair c][dim][8]: tokens 4c..4c+3 (set a) then 16+4c..16+4c+3
-  // (set b), which is one lane's whole p.V operand for that dim
+  uint16_t k[2][(D / 8) * kStep * 8];  // [slice][token][8], tokens of one step
+  // [quad pair c][dim][8]: quad pair c = 2m + h holds quads 4m+h (elements
+  // 0..3) and 4m+2+h (4..7), which is one lane's whole p.V operand for that
+  // dim (PrefillEngine)
   uint16_t v[2][(kStep / 8) * D * 8];
 };
 
 // One workgroup tile: positions x*kWaves*pos_per_wave .. of chunk c, kv head g.
 // Every branch that returns early is uniform over the workgroup, and every
 // path that reaches the step loop runs the same barriers in every wave.
-template <int D, int BS, int NT>
+template <int D, int BS>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D>& smem, int x,
                                              int c, int g) {
-  using Eng = Bf16Engine<D, BS, NT>;
-  constexpr int KS = Eng::KS, VT = Eng::VT;
+  using Eng = PrefillEngine<D>;
+  constexpr int KS = Eng::KS, DB = Eng::DB;
   constexpr int kChunks = 2 * D * kStep * 2 / 16;  // 16-byte pieces of one step's K and V
   constexpr int kPer = kChunks / 256;              // per thread
   static_assert(kChunks % 256 == 0, "a step is a whole number of 16-byte pieces per thread");
   int q0, L, prior;
   if (!chunk_geometry(a, c, a.mb * BS, q0, L, prior)) return;  // uniform per workgroup
   const int G = a.hq / a.hkv;
-  const int pos_per_wave = 16 * NT / G;
+  const int pos_per_wave = kPrefillRows / G;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wg_i0 = x * kWaves * pos_per_wave;
   if (wg_i0 >= L) return;  // uniform per workgroup
   const int i0 = wg_i0 + wave * pos_per_wave;
-  const int r = lane & 15, kg = lane >> 4;
+  const int r = lane & 31, h = lane >> 5;
   const uint16_t* pool = static_cast<const uint16_t*>(a.pool);
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   // the two LDS buffers, through pointers that alias nothing else
@@ -1690,14 +1826,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
 
   Eng eng;
   eng.init();
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int R = nt * 16 + r;
-    const int i = i0 + R / G, h = R - (R / G) * G;
-    if (i < L) {
-      eng.load_q(nt, q + ((static_cast<int64_t>(q0) + i) * a.hq + g * G + h) * D, kg);
-      eng.lim[nt] = prior + i;
-    }
+  // this lane's row: position i, head hd
+  const int i = i0 + r / G, hd = r - (r / G) * G;
+  if (i < L) {
+    eng.load_q(q + ((static_cast<int64_t>(q0) + i) * a.hq + g * G + hd) * D, h);
+    eng.lim = prior + i;
   }
   // keys 0 .. kend-1 for this wave's rows, kend_wg for the workgroup's
   const int kend = prior + min(L, i0 + pos_per_wave);
@@ -1707,10 +1840,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
   const int64_t vofs = static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(g) * D * BS;
 
   // Piece p of a step: K pieces first ([slice c][token t], one token's 8
-  // dims), then V pieces: 2 dims x 4 tokens of one 4-token slice, where
-  // V piece 2m + h is dim pair m % (D/2) of slice pair m / (D/2), set h
-  // (a: tokens 4c.., b: tokens 16+4c..). Adjacent lanes thus hold the two sets
-  // of the same two dims, which the stash turns into two whole LDS rows.
+  // dims), then V pieces: 2 dims x 4 tokens of one quad (the pool's V layout
+  // is [quad][dim][4]). V piece 2m + w is dim pair m % (D/2) of quad pair
+  // cp = m / (D/2), quad 4(cp/2) + cp%2 + 2w of the step. Adjacent lanes thus
+  // hold the two quads of the same two dims, which the stash turns into two
+  // whole LDS rows.
   // Returns the element offset inside the step's block (A: tokens 0..15 or,
   // at bs 32, all 32) and whether it comes from block B (bs 16, tokens 16..31).
   auto piece_src = [&](int u, int pc, bool& from_b) -> int64_t {
@@ -1723,10 +1857,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
     const int pv = pc - kChunks / 2;
     const int m = pv >> 1;
     const int cp = m / (D / 2), dp = m - cp * (D / 2);
-    const int sl = cp + 4 * (pv & 1);
-    from_b = BS == 16 && sl >= 4;
-    const int bsl = BS == 16 ? (sl & 3) : sl;
-    return vofs + (static_cast<int64_t>(bsl) * D + 2 * dp) * 4;
+    const int quad = 4 * (cp >> 1) + (cp & 1) + 2 * (pv & 1);
+    from_b = BS == 16 && quad >= 4;
+    const int bq = BS == 16 ? (quad & 3) : quad;
+    return vofs + (static_cast<int64_t>(bq) * D + 2 * dp) * 4;
   };
   // Steps are fetched two ahead: step s+2's loads go out while step s is
   // computed, and step s+1, loaded during step s-1, is stored to LDS after it.
@@ -1735,10 +1869,27 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
   // step's addresses into a buffer nobody reads), which keeps the compiler's
   // wait for step s+1 exact instead of a wait for every load in flight.
   const int nsteps = (kend_wg + kStep - 1) / kStep;
-  auto fetch = [&](int step, u32x4 (&pre)[kPer]) {  // step -> registers
+  // The block-table entries of a step (its block, and at bs 16 the block of
+  // tokens 16..31) are read one iteration before the step's loads go out, by
+  // vector loads issued ahead of the previous step's K/V loads: so they are
+  // in registers by the time they are used, and waiting for them never waits
+  // for a K/V load (the loads complete in order). A scalar load would be
+  // waited for together with the LDS operations in flight.
+  const auto trsrc = tile_rsrc(trow, a.mb * 4);
+  struct Ent {
+    int a, b;
+  };
+  auto load_ent = [&](int step) -> Ent {
     const int t0 = min(step, nsteps - 1) * kStep;
-    const int ia = table_entry(trow, t0 / BS);
-    const int ib = (BS == 16 && t0 + 16 < kend_wg) ? table_entry(trow, t0 / BS + 1) : ia;
+    const int ia = t0 / BS;
+    const int ib = (BS == 16 && t0 + 16 < kend_wg) ? ia + 1 : ia;
+    return Ent{static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(trsrc, 4 * ia, 0, 0)),
+               BS == 16 ? static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(trsrc, 4 * ib, 0, 0))
+                        : 0};
+  };
+  auto fetch = [&](const Ent& e, u32x4 (&pre)[kPer]) {  // step -> registers
+    const int ia = __builtin_amdgcn_readfirstlane(e.a);
+    const int ib = BS == 16 ? __builtin_amdgcn_readfirstlane(e.b) : ia;
     const uint16_t* bA = pool + clamp_block(ia, a.nb) * a.blk_elems;
     const uint16_t* bB = pool + clamp_block(ib, a.nb) * a.blk_elems;
 #pragma unroll
@@ -1759,14 +1910,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
       if (u < kPer / 2) {
         *reinterpret_cast<u32x4*>(&lk[buf * kK + pc * 8]) = pre[u];
       } else {
-        // 4 tokens of dims 2dp and 2dp+1 of set `odd` of slice pair cp, 8
-        // bytes each. Adjacent lanes hold the two sets of the same dims, so
-        // each store instruction fills whole 16-byte rows pairwise (a 2-way
-        // bank pattern; one lane per row pair would be 8-way).
+        // 4 tokens of dims 2dp and 2dp+1 of quad half `w` of quad pair cp,
+        // 8 bytes each. Adjacent lanes hold the two halves of the same dims,
+        // so each store instruction fills whole 16-byte rows pairwise (a
+        // 2-way bank pattern; one lane per row pair would be 8-way).
         const int pv = pc - kChunks / 2;
-        const int m = pv >> 1, odd = pv & 1;
+        const int m = pv >> 1, w = pv & 1;
         const int cp = m / (D / 2), dp = m - cp * (D / 2);
-        uint16_t* row = &lv[buf * kV + (cp * D + 2 * dp) * 8 + odd * 4];
+        uint16_t* row = &lv[buf * kV + (cp * D + 2 * dp) * 8 + w * 4];
         *reinterpret_cast<u32x2*>(row) = u32x2{pre[u][0], pre[u][1]};
         *reinterpret_cast<u32x2*>(row + 8) = u32x2{pre[u][2], pre[u][3]};
       }
@@ -1775,36 +1926,52 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
   // One step from LDS: the K operands feed the scores, then the V operands are
   // read into registers the K operands no longer need while the softmax runs.
   // EDGE: the step may reach past the end of the keys or past some row's
-  // limit (see Bf16Engine::finish).
+  // limit (see PrefillEngine::edge_masks).
   auto step = [&]<bool EDGE>(int buf, int t0) {
-    u32x4 kA[KS], kB[KS];
+    u32x4 kop[KS];
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
-      kA[s2] = *reinterpret_cast<const u32x4*>(&lk[buf * kK + ((4 * s2 + kg) * kStep + r) * 8]);
-      kB[s2] = *reinterpret_cast<const u32x4*>(&lk[buf * kK + ((4 * s2 + kg) * kStep + 16 + r) * 8]);
-    }
-    f32x4 sa[NT], sb[NT];
-    eng.scores(kA, kB, sa, sb);
-    u32x4 vv[VT];
+    for (int s2 = 0; s2 < KS; ++s2)
+      kop[s2] = *reinterpret_cast<const u32x4*>(&lk[buf * kK + ((2 * s2 + h) * kStep + r) * 8]);
+    f32x16 sc = eng.scores(kop);
+    // every K operand read goes out before the first score MFMA: the MFMAs
+    // form one dependent chain, and a read issued just before its MFMA would
+    // add an LDS latency to each link
+    __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);  // MFMAs
+    __builtin_amdgcn_sched_barrier(0);  // (the V reads below stay out of that group)
+    u32x4 vv[2 * DB];
 #pragma unroll
-    for (int j = 0; j < VT; ++j)
-      vv[j] = *reinterpret_cast<const u32x4*>(&lv[buf * kV + (kg * D + 16 * j + r) * 8]);
-    eng.template finish<EDGE>(sa, sb, vv, t0, kend_wg, lane, a.sl2e);
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int mh = 0; mh < 2; ++mh)
+        vv[2 * db + mh] =
+            *reinterpret_cast<const u32x4*>(&lv[buf * kV + ((2 * mh + h) * D + 32 * db + r) * 8]);
+    if constexpr (EDGE) eng.edge_masks(sc, vv, t0, kend_wg, h);
+    eng.softmax_pv(sc, vv, a.sl2e);
   };
-  // Iteration s: fetch step s+2 into `fetch_into` (free: its step s went to
-  // LDS in iteration s-1), compute step s from LDS buffer s&1, store step s+1
-  // from `held` into LDS buffer (s+1)&1 (last read in iteration s-1, before
-  // its barrier), then one barrier.
+  // Iteration s: read the table entries of step s+3 and fetch step s+2 into
+  // `fetch_into` (free: its step s went to LDS in iteration s-1), compute
+  // step s from LDS buffer s&1, store step s+1 from `held` into LDS buffer
+  // (s+1)&1 (last read in iteration s-1, before its barrier), then one
+  // barrier.
+  Ent ent_next;  // entries of step s+2 in iteration s
   auto iteration = [&]<bool EDGE>(int s, u32x4 (&fetch_into)[kPer], const u32x4 (&held)[kPer]) {
-    fetch(s + 2, fetch_into);
     const int t0 = s * kStep;
-    if (s < nsteps && i0 < L && t0 < kend) step.template operator()<EDGE>(s & 1, t0);
+    const int buf = s & 1;
+    const Ent e = ent_next;
+    ent_next = load_ent(s + 3);
+    fetch(e, fetch_into);
+    if (s < nsteps && i0 < L && t0 < kend) step.template operator()<EDGE>(buf, t0);  // uniform
     stash((s + 1) & 1, held);
     __syncthreads();
   };
   u32x4 preA[kPer], preB[kPer];
-  fetch(0, preA);
-  fetch(1, preB);
+  {
+    const Ent e0 = load_ent(0), e1 = load_ent(1);
+    ent_next = load_ent(2);
+    fetch(e0, preA);
+    fetch(e1, preB);
+  }
   stash(0, preA);
   __syncthreads();
   // Steps before `inner` lie wholly before the end of the keys and at or
@@ -1823,33 +1990,26 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
     iteration.template operator()<true>(s, preA, preB);
     iteration.template operator()<true>(s + 1, preB, preA);
   }
-  uint16_t* out = static_cast<uint16_t*>(a.out);
+  const float lt = eng.l + __shfl_xor(eng.l, 32);  // both halves of the row
+  if (i >= L) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  uint16_t* orow = static_cast<uint16_t*>(a.out) +
+                   ((static_cast<int64_t>(q0) + i) * a.hq + g * G + hd) * D;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const float lt = sum_over_groups(eng.l[nt]);
-    const int R = nt * 16 + r;
-    const int i = i0 + R / G, h = R - (R / G) * G;
-    if (i >= L) continue;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* orow = out + ((static_cast<int64_t>(q0) + i) * a.hq + g * G + h) * D;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      u32x2 w;
-      w[0] = f32_to_bf16_bits(eng.o[nt][j][0] * inv) |
-             (static_cast<uint32_t>(f32_to_bf16_bits(eng.o[nt][j][1] * inv)) << 16);
-      w[1] = f32_to_bf16_bits(eng.o[nt][j][2] * inv) |
-             (static_cast<uint32_t>(f32_to_bf16_bits(eng.o[nt][j][3] * inv)) << 16);
-      *reinterpret_cast<u32x2*>(orow + 16 * j + 4 * kg) = w;
-    }
-  }
+    for (int p = 0; p < 4; ++p)
+      store4<uint16_t>(orow + 32 * db + 8 * p + 4 * h,
+                       f32x4{eng.o[db][4 * p], eng.o[db][4 * p + 1], eng.o[db][4 * p + 2],
+                             eng.o[db][4 * p + 3]} * inv);
 }
 
 // One workgroup per tile, in grid order: (x, chunk, kv head) = blockIdx.
-template <int D, int BS, int NT>
+template <int D, int BS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillArgs a) {
   __shared__ PrefillSmem<D> sm;
-  prefill_tile<D, BS, NT>(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+  prefill_tile<D, BS>(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Tiles in longest-first order. A tile's work is its number of 32-token key
@@ -1870,12 +2030,12 @@ struct PrefillLds {
 
 // Ranks the (chunk, x) pairs by their number of key steps; returns how many
 // pairs there are. Ends with a barrier.
-template <int BS, int NT>
+template <int BS>
 __device__ __forceinline__ int prefill_rank(const PrefillArgs& a, int gx, int* __restrict__ key_of,
                                             int* __restrict__ order) {
   const int M = a.num_chunks * gx;
   const int G = a.hq / a.hkv;
-  const int pos_per_wg = kWaves * 16 * NT / G;
+  const int pos_per_wg = kWaves * kPrefillRows / G;
   for (int i = threadIdx.x; i < M; i += kWaves * 64) {
     const int c = i / gx, x = i - c * gx;
     int q0, L, prior, key = 0;
@@ -1897,13 +2057,13 @@ __device__ __forceinline__ int prefill_rank(const PrefillArgs& a, int gx, int* _
   return M;
 }
 
-template <int D, int BS, int NT>
+template <int D, int BS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_lpt_kernel(PrefillArgs a, int gx) {
   __shared__ PrefillSmem<D> sm;
   __shared__ int s_key[kMaxPrefillTiles];
   __shared__ int s_order[kMaxPrefillTiles];
-  const int tiles = prefill_rank<BS, NT>(a, gx, s_key, s_order) * a.hkv;
+  const int tiles = prefill_rank<BS>(a, gx, s_key, s_order) * a.hkv;
   const int P = static_cast<int>(gridDim.x);
   for (int k = 0; k * P < tiles; ++k) {
     const int t = k * P + ((k & 1) ? P - 1 - static_cast<int>(blockIdx.x)
@@ -1911,7 +2071,7 @@ void prefill_bf16_lpt_kernel(PrefillArgs a, int gx) {
     if (t >= tiles) break;
     const int combo = s_order[t / a.hkv];
     if (s_key[combo] == 0) break;  // sorted: every later tile is empty too
-    prefill_tile<D, BS, NT>(a, sm, combo % gx, combo / gx, t % a.hkv);
+    prefill_tile<D, BS>(a, sm, combo % gx, combo / gx, t % a.hkv);
   }
 }
 
@@ -1934,11 +2094,11 @@ union MixedSmem {
   PrefillLds<D> p;
 };
 
-template <int D, int BS, int NT>
+template <int D, int BS>
 __device__ __forceinline__ void prefill_from_queue(const PrefillArgs& a, int gx,
                                                    int32_t* __restrict__ queue,
                                                    PrefillLds<D>& ps) {
-  const int tiles = prefill_rank<BS, NT>(a, gx, ps.key, ps.order) * a.hkv;
+  const int tiles = prefill_rank<BS>(a, gx, ps.key, ps.order) * a.hkv;
   for (;;) {
     if (threadIdx.x == 0) ps.next = atomicAdd(&queue[2], 1);
     __syncthreads();
@@ -1947,18 +2107,18 @@ __device__ __forceinline__ void prefill_from_queue(const PrefillArgs& a, int gx,
     if (t >= tiles) break;
     const int combo = ps.order[t / a.hkv];
     if (ps.key[combo] == 0) break;  // sorted: every later tile is empty too
-    prefill_tile<D, BS, NT>(a, ps.sm, combo % gx, combo / gx, t % a.hkv);
+    prefill_tile<D, BS>(a, ps.sm, combo % gx, combo / gx, t % a.hkv);
   }
 }
 
-template <int D, int BS, int NT>
+template <int D, int BS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mixed_bf16_kernel(DecodeArgs da, PrefillArgs pa, int gx, int32_t* __restrict__ queue) {
   __shared__ MixedSmem<D> u;
   const int half = gridDim.x / 2;
   const bool prefill_first = blockIdx.x < half;
   if (prefill_first) {
-    if (pa.num_chunks > 0) prefill_from_queue<D, BS, NT>(pa, gx, queue, u.p);
+    if (pa.num_chunks > 0) prefill_from_queue<D, BS>(pa, gx, queue, u.p);
     __syncthreads();  // LDS changes hands
     if (da.num_seqs > 0) decode_persistent<D, BS>(da, queue, u.d, -1, gridDim.x - half);
   } else {
@@ -1966,7 +2126,7 @@ void mixed_bf16_kernel(DecodeArgs da, PrefillArgs pa, int gx, int32_t* __restric
     if (da.num_seqs > 0)
       decode_persistent<D, BS>(da, queue, u.d, blockIdx.x - half, gridDim.x - half);
     __syncthreads();
-    if (pa.num_chunks > 0) prefill_from_queue<D, BS, NT>(pa, gx, queue, u.p);
+    if (pa.num_chunks > 0) prefill_from_queue<D, BS>(pa, gx, queue, u.p);
   }
   leave_queue(queue);
 }
@@ -2228,24 +2388,22 @@ hipError_t launch_decode_f32(const DecodeArgs& a, int G, int grid, hipStream_t s
   return hipGetLastError();
 }
 
-constexpr int kPrefillNT = 2;
-
 template <int D, int BS>
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int max_chunk_len, hipStream_t st) {
   const int G = a.hq / a.hkv;
-  const int pos_per_wg = kWaves * 16 * kPrefillNT / G;
+  const int pos_per_wg = kWaves * kPrefillRows / G;
   const int gx = (max_chunk_len + pos_per_wg - 1) / pos_per_wg;
   const int64_t combos = static_cast<int64_t>(gx) * a.num_chunks;
   if (combos <= kMaxPrefillTiles) {
-    static const int resident = resident_workgroups(prefill_bf16_lpt_kernel<D, BS, kPrefillNT>);
+    static const int resident = resident_workgroups(prefill_bf16_lpt_kernel<D, BS>);
     const int64_t tiles = combos * a.hkv;
     const int64_t cap = resident > 0 ? resident : 512;
     const int w = static_cast<int>(tiles < cap ? tiles : cap);
-    hipLaunchKernelGGL((prefill_bf16_lpt_kernel<D, BS, kPrefillNT>), dim3(w), dim3(256), 0, st,
+    hipLaunchKernelGGL((prefill_bf16_lpt_kernel<D, BS>), dim3(w), dim3(256), 0, st,
                        a, gx);
   } else {
     dim3 grid(gx, a.num_chunks, a.hkv);
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, BS, kPrefillNT>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, BS>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -2377,9 +2535,9 @@ PrefillArgs prefill_args(void* out, const void* q, const void* pool, const int32
 template <int D, int BS>
 hipError_t launch_mixed_bf16(const DecodeArgs& da, const PrefillArgs& pa, int gx, int32_t* queue,
                              hipStream_t st) {
-  static const int resident = resident_workgroups(mixed_bf16_kernel<D, BS, kPrefillNT>);
+  static const int resident = resident_workgroups(mixed_bf16_kernel<D, BS>);
   // (the persistent decode inside merges its split-K partitions itself)
-  hipLaunchKernelGGL((mixed_bf16_kernel<D, BS, kPrefillNT>), dim3(resident > 0 ? resident : 512),
+  hipLaunchKernelGGL((mixed_bf16_kernel<D, BS>), dim3(resident > 0 ? resident : 512),
                      dim3(256), 0, st, da, pa, gx, queue);
   return hipGetLastError();
 }
@@ -2505,7 +2663,7 @@ hipError_t launch_mixed(void* dec_out, const void* dec_q, const void* pool,
                         int pre_max_blocks, int num_q_heads, const PoolShape& ps, float scale,
                         int dtype, void* workspace, hipStream_t st) {
   const int G = num_q_heads / ps.num_kv_heads;
-  const int pos_per_wg = kWaves * 16 * kPrefillNT / G;
+  const int pos_per_wg = kWaves * kPrefillRows / G;
   const int64_t gx = num_chunks > 0 ? (max_chunk_len + pos_per_wg - 1) / pos_per_wg : 0;
   const bool fused = dtype == 1 && num_seqs <= kMaxScanSeqs && gx * num_chunks <= kMaxPrefillTiles;
   if (!fused || num_seqs == 0 || num_chunks == 0 || max_chunk_len == 0) {
