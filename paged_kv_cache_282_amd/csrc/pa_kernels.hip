@@ -1796,24 +1796,30 @@ struct PrefillSmem {
   uint16_t v[2][(kStep / 8) * D * 8];
 };
 
-// One workgroup tile: positions x*kWaves*pos_per_wave .. of chunk c, kv head g.
+// Waves of a prefill workgroup (W): at d 128 eight (two per SIMD, 256 rows
+// sharing each step's K and V), at d 64 four (a step's 512 pieces are then
+// one K and one V piece per thread).
+constexpr int prefill_waves(int D) { return D == 128 ? 8 : kWaves; }
+
+// One workgroup tile: positions x*W*pos_per_wave .. of chunk c, kv head g.
 // Every branch that returns early is uniform over the workgroup, and every
 // path that reaches the step loop runs the same barriers in every wave.
-template <int D, int BS>
+template <int D, int BS, int W>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D>& smem, int x,
                                              int c, int g) {
   using Eng = PrefillEngine<D>;
   constexpr int KS = Eng::KS, DB = Eng::DB;
+  constexpr int kThreads = 64 * W;
   constexpr int kChunks = 2 * D * kStep * 2 / 16;  // 16-byte pieces of one step's K and V
-  constexpr int kPer = kChunks / 256;              // per thread
-  static_assert(kChunks % 256 == 0, "a step is a whole number of 16-byte pieces per thread");
+  constexpr int kPer = kChunks / kThreads;         // per thread
+  static_assert(kChunks % kThreads == 0, "a step is a whole number of 16-byte pieces per thread");
   int q0, L, prior;
   if (!chunk_geometry(a, c, a.mb * BS, q0, L, prior)) return;  // uniform per workgroup
   const int G = a.hq / a.hkv;
   const int pos_per_wave = kPrefillRows / G;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wg_i0 = x * kWaves * pos_per_wave;
+  const int wg_i0 = x * W * pos_per_wave;
   if (wg_i0 >= L) return;  // uniform per workgroup
   const int i0 = wg_i0 + wave * pos_per_wave;
   const int r = lane & 31, h = lane >> 5;
@@ -1834,7 +1840,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
   }
   // keys 0 .. kend-1 for this wave's rows, kend_wg for the workgroup's
   const int kend = prior + min(L, i0 + pos_per_wave);
-  const int kend_wg = prior + min(L, wg_i0 + kWaves * pos_per_wave);
+  const int kend_wg = prior + min(L, wg_i0 + W * pos_per_wave);
   const int32_t* trow = a.tables + static_cast<int64_t>(c) * a.mb;
   const int64_t kofs = static_cast<int64_t>(g) * BS * D;
   const int64_t vofs = static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(g) * D * BS;
@@ -1895,18 +1901,18 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       bool from_b;
-      const int64_t off = piece_src(u, u * 256 + static_cast<int>(threadIdx.x), from_b);
+      const int64_t off = piece_src(u, u * kThreads + static_cast<int>(threadIdx.x), from_b);
       pre[u] = ld16((from_b ? bB : bA) + off);
     }
   };
   // Pieces u < kPer / 2 of a thread are K pieces and the rest V pieces (the
   // first kChunks / 2 piece numbers are K's); deciding by u keeps the choice
   // out of the per-lane code.
-  static_assert(kChunks / 2 == (kPer / 2) * 256, "K pieces are the first half of every thread's");
+  static_assert(kChunks / 2 == (kPer / 2) * kThreads, "K pieces are the first half of every thread's");
   auto stash = [&](int buf, const u32x4 (&pre)[kPer]) {  // registers -> LDS buffer
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int pc = u * 256 + static_cast<int>(threadIdx.x);
+      const int pc = u * kThreads + static_cast<int>(threadIdx.x);
       if (u < kPer / 2) {
         *reinterpret_cast<u32x4*>(&lk[buf * kK + pc * 8]) = pre[u];
       } else {
@@ -2006,10 +2012,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, PrefillSmem<D
 
 // One workgroup per tile, in grid order: (x, chunk, kv head) = blockIdx.
 template <int D, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * prefill_waves(D)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillArgs a) {
   __shared__ PrefillSmem<D> sm;
-  prefill_tile<D, BS>(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
+  prefill_tile<D, BS, prefill_waves(D)>(a, sm, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Tiles in longest-first order. A tile's work is its number of 32-token key
@@ -2030,13 +2036,13 @@ struct PrefillLds {
 
 // Ranks the (chunk, x) pairs by their number of key steps; returns how many
 // pairs there are. Ends with a barrier.
-template <int BS>
+template <int BS, int W>
 __device__ __forceinline__ int prefill_rank(const PrefillArgs& a, int gx, int* __restrict__ key_of,
                                             int* __restrict__ order) {
   const int M = a.num_chunks * gx;
   const int G = a.hq / a.hkv;
-  const int pos_per_wg = kWaves * kPrefillRows / G;
-  for (int i = threadIdx.x; i < M; i += kWaves * 64) {
+  const int pos_per_wg = W * kPrefillRows / G;
+  for (int i = threadIdx.x; i < M; i += W * 64) {
     const int c = i / gx, x = i - c * gx;
     int q0, L, prior, key = 0;
     if (chunk_geometry(a, c, a.mb * BS, q0, L, prior) && x * pos_per_wg < L)
@@ -2044,7 +2050,7 @@ __device__ __forceinline__ int prefill_rank(const PrefillArgs& a, int gx, int* _
     key_of[i] = key;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < M; i += kWaves * 64) {
+  for (int i = threadIdx.x; i < M; i += W * 64) {
     const int ki = key_of[i];
     int rank = 0;
     for (int j = 0; j < M; ++j) {
@@ -2058,12 +2064,13 @@ __device__ __forceinline__ int prefill_rank(const PrefillArgs& a, int gx, int* _
 }
 
 template <int D, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * prefill_waves(D)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_lpt_kernel(PrefillArgs a, int gx) {
+  constexpr int W = prefill_waves(D);
   __shared__ PrefillSmem<D> sm;
   __shared__ int s_key[kMaxPrefillTiles];
   __shared__ int s_order[kMaxPrefillTiles];
-  const int tiles = prefill_rank<BS>(a, gx, s_key, s_order) * a.hkv;
+  const int tiles = prefill_rank<BS, W>(a, gx, s_key, s_order) * a.hkv;
   const int P = static_cast<int>(gridDim.x);
   for (int k = 0; k * P < tiles; ++k) {
     const int t = k * P + ((k & 1) ? P - 1 - static_cast<int>(blockIdx.x)
@@ -2071,7 +2078,7 @@ void prefill_bf16_lpt_kernel(PrefillArgs a, int gx) {
     if (t >= tiles) break;
     const int combo = s_order[t / a.hkv];
     if (s_key[combo] == 0) break;  // sorted: every later tile is empty too
-    prefill_tile<D, BS>(a, sm, combo % gx, combo / gx, t % a.hkv);
+    prefill_tile<D, BS, W>(a, sm, combo % gx, combo / gx, t % a.hkv);
   }
 }
 
@@ -2098,7 +2105,7 @@ template <int D, int BS>
 __device__ __forceinline__ void prefill_from_queue(const PrefillArgs& a, int gx,
                                                    int32_t* __restrict__ queue,
                                                    PrefillLds<D>& ps) {
-  const int tiles = prefill_rank<BS>(a, gx, ps.key, ps.order) * a.hkv;
+  const int tiles = prefill_rank<BS, kWaves>(a, gx, ps.key, ps.order) * a.hkv;
   for (;;) {
     if (threadIdx.x == 0) ps.next = atomicAdd(&queue[2], 1);
     __syncthreads();
@@ -2107,7 +2114,7 @@ __device__ __forceinline__ void prefill_from_queue(const PrefillArgs& a, int gx,
     if (t >= tiles) break;
     const int combo = ps.order[t / a.hkv];
     if (ps.key[combo] == 0) break;  // sorted: every later tile is empty too
-    prefill_tile<D, BS>(a, ps.sm, combo % gx, combo / gx, t % a.hkv);
+    prefill_tile<D, BS, kWaves>(a, ps.sm, combo % gx, combo / gx, t % a.hkv);
   }
 }
 
@@ -2322,14 +2329,15 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const uint8_t* __restr
 // ---------------------------------------------------------------------------
 // Dispatch helpers.
 // ---------------------------------------------------------------------------
-// Workgroups that fit on the device at once for `kernel` (0 if unknown).
+// Workgroups of `threads` threads that fit on the device at once for `kernel`
+// (0 if unknown).
 template <typename K>
-int resident_workgroups(K kernel) {
+int resident_workgroups(K kernel, int threads = 256) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
     return 0;
   return cus * per_cu;
 }
@@ -2391,19 +2399,20 @@ hipError_t launch_decode_f32(const DecodeArgs& a, int G, int grid, hipStream_t s
 template <int D, int BS>
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int max_chunk_len, hipStream_t st) {
   const int G = a.hq / a.hkv;
-  const int pos_per_wg = kWaves * kPrefillRows / G;
+  constexpr int W = prefill_waves(D);
+  const int pos_per_wg = W * kPrefillRows / G;
   const int gx = (max_chunk_len + pos_per_wg - 1) / pos_per_wg;
   const int64_t combos = static_cast<int64_t>(gx) * a.num_chunks;
   if (combos <= kMaxPrefillTiles) {
-    static const int resident = resident_workgroups(prefill_bf16_lpt_kernel<D, BS>);
+    static const int resident = resident_workgroups(prefill_bf16_lpt_kernel<D, BS>, 64 * W);
     const int64_t tiles = combos * a.hkv;
     const int64_t cap = resident > 0 ? resident : 512;
     const int w = static_cast<int>(tiles < cap ? tiles : cap);
-    hipLaunchKernelGGL((prefill_bf16_lpt_kernel<D, BS>), dim3(w), dim3(256), 0, st,
+    hipLaunchKernelGGL((prefill_bf16_lpt_kernel<D, BS>), dim3(w), dim3(64 * W), 0, st,
                        a, gx);
   } else {
     dim3 grid(gx, a.num_chunks, a.hkv);
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, BS>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, BS>), grid, dim3(64 * W), 0, st, a);
   }
   return hipGetLastError();
 }
