@@ -177,6 +177,7 @@ __device__ __forceinline__ int clamp_block(int blk, int64_t nb) {
 // How far (in base-2 exponent) the running maximum may pass the reference
 // maximum before the softmax state is rescaled; weights stay below 2^8.
 constexpr float kRescaleSlack = 8.f;
+constexpr float kSlackWeight = 256.f;  // 2^kRescaleSlack
 // The reference maximum of a row that has seen no key yet: finite, so that
 // exp2(s - m) needs no special case before the first key (it is 0 for every
 // masked score), and a state with l = 0 adds nothing wherever states merge.
@@ -1708,41 +1709,61 @@ struct PrefillEngine {
     }
   }
 
-  // Online softmax and p.V on scores already masked (see Bf16Engine for the
-  // rescale slack and the bf16 weight sums).
-  __device__ __forceinline__ void softmax_pv(const f32x16& sc, const u32x4 (&vv)[2 * DB],
-                                             float sl2e) {
-    float mx = sc[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = smax(mx, sc[e]);
-    {  // the other half of the row (lane ^ 32)
-      const uint32_t u = __float_as_uint(mx);
-      const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-      mx = smax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mtop = smax(m, mx * sl2e);
-    const bool grow = mtop > m + kRescaleSlack;
-    const float mnew = grow ? mtop : m;
-    bf16x8 p[2];
+  // bf16 weights exp2(s * sl2e - mref) of this lane's 16 scores, and their sum
+  // (two chains of four bf16 pair sums).
+  __device__ __forceinline__ float weights(const f32x16& sc, float sl2e, float mref,
+                                           bf16x8 (&p)[2]) const {
 #pragma unroll
     for (int e = 0; e < 16; ++e)
-      p[e >> 3][e & 7] = static_cast<__bf16>(exp2_fast(fmaf(sc[e], sl2e, -mnew)));
-    float ps = 0.f;
+      p[e >> 3][e & 7] = static_cast<__bf16>(exp2_fast(fmaf(sc[e], sl2e, -mref)));
+    float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int mh = 0; mh < 2; ++mh) {
-      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[mh], p[mh], 0, 1), kOnes2, ps, false);
-      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[mh], p[mh], 2, 3), kOnes2, ps, false);
-      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[mh], p[mh], 4, 5), kOnes2, ps, false);
-      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[mh], p[mh], 6, 7), kOnes2, ps, false);
+      ps[mh] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[mh], p[mh], 0, 1), kOnes2, ps[mh], false);
+      ps[mh] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[mh], p[mh], 2, 3), kOnes2, ps[mh], false);
+      ps[mh] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[mh], p[mh], 4, 5), kOnes2, ps[mh], false);
+      ps[mh] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p[mh], p[mh], 6, 7), kOnes2, ps[mh], false);
     }
-    if (__builtin_amdgcn_ballot_w64(grow && m != kNoMax) != 0) {
-      const float alpha = exp2_fast(m - mnew);
-      l *= alpha;
+    return ps[0] + ps[1];
+  }
+
+  // Online softmax and p.V on scores already masked (see Bf16Engine for the
+  // rescale slack and the bf16 weight sums). The weights are first taken
+  // against the row's reference maximum m. Every weight is non-negative and at
+  // most its lane's sum, so while every lane's sum stays below 2^kRescaleSlack
+  // no score has passed m + kRescaleSlack, the state needs no rescale, and the
+  // row's maximum is not needed at all. Otherwise (a row's first keys, whose m
+  // is kNoMax, make the sums infinite; so does a NaN) the wave takes the
+  // maximum and applies the rescale rule, recomputing the weights of the rows
+  // whose reference moves.
+  __device__ __forceinline__ void softmax_pv(const f32x16& sc, const u32x4 (&vv)[2 * DB],
+                                             float sl2e) {
+    bf16x8 p[2];
+    float ps = weights(sc, sl2e, m, p);
+    if (__builtin_amdgcn_ballot_w64(!(ps < kSlackWeight)) != 0) {  // wave-uniform
+      float mx = sc[0];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      for (int e = 1; e < 16; ++e) mx = smax(mx, sc[e]);
+      {  // the other half of the row (lane ^ 32)
+        const uint32_t u = __float_as_uint(mx);
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        mx = smax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float mtop = smax(m, mx * sl2e);
+      const bool grow = mtop > m + kRescaleSlack;
+      const float mnew = grow ? mtop : m;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        ps = weights(sc, sl2e, mnew, p);  // rows that keep m get the same weights
+        if (__builtin_amdgcn_ballot_w64(grow && m != kNoMax) != 0) {
+          const float alpha = exp2_fast(m - mnew);
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        }
+      }
+      m = mnew;
     }
     l += ps;
-    m = mnew;
 #pragma unroll
     for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
