@@ -97,7 +97,61 @@ def parse():
                     help="after the headline, copy half of the first layer's pool onto the "
                          "other half with one pa_copy_blocks call (a copy of known size for "
                          "scaling memory-traffic counters)")
+    ap.add_argument("--loop", choices=("decode", "prefill", "mixed"),
+                    help="instead of measuring, run one call of the mixed iteration (its "
+                         "decode, its prefill, or both in one pa_mixed_attention call) back to "
+                         "back for --loop-seconds, printing a line a second: a steady load for "
+                         "sampling power and clocks from outside")
+    ap.add_argument("--loop-seconds", type=float, default=20.0)
     return ap.parse_args()
+
+
+def loop_calls(pa, torch, make_workload, which: str, seconds: float) -> dict:
+    """One call of the mixed iteration back to back (pool after the iteration's append)."""
+    w = make_workload("mixed")
+    pool = to_dev(w.pool, w.dtype, torch)
+    pa.pa_append_kv(pool, to_dev(w.k_new, w.dtype, torch), to_dev(w.v_new, w.dtype, torch),
+                    i32(w.slot_mapping, torch), w.block_size)
+    q, tables, lens = to_dev(w.q, w.dtype, torch), i32(w.block_tables, torch), \
+        i32(w.context_lens, torch)
+    out = torch.empty_like(q)
+    ws = pa.new_decode_workspace(w.num_seqs, w.num_q_heads, w.head_dim, w.max_context_len)
+    pq = to_dev(w.prefill_q, w.dtype, torch)
+    pout = torch.empty_like(pq)
+    pt, pl = i32(w.prefill_block_tables, torch), i32(w.prefill_context_lens, torch)
+    qsl = i32(w.query_start_loc, torch)
+    max_chunk = int(np.diff(w.query_start_loc).max())
+
+    def decode():
+        pa.pa_decode(out, q, pool, tables, lens, w.max_context_len, w.num_kv_heads,
+                     w.block_size, w.scale, ws)
+
+    def prefill():
+        pa.pa_prefill_chunk(pout, pq, pool, pt, pl, qsl, max_chunk, w.num_kv_heads,
+                            w.block_size, w.scale)
+
+    def mixed():
+        pa.pa_mixed_attention(out, q, tables, lens, w.max_context_len, pout, pq, pt, pl, qsl,
+                              max_chunk, pool, w.num_kv_heads, w.block_size, w.scale, ws)
+
+    fn = {"decode": decode, "prefill": prefill, "mixed": mixed}[which]
+    fn()
+    torch.cuda.synchronize()
+    log(f"looping {which} for {seconds:.0f} s")
+    n, t0, last = 0, time.time(), time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        n += 20
+        if time.time() - last >= 1.0:
+            last = time.time()
+            log(f"  {which}: {n} calls, {(last - t0) / n * 1e6:.1f} us per call")
+    dt = time.time() - t0
+    return {"loop": which, "calls": n, "seconds": round(dt, 2),
+            "us_per_call": round(dt / n * 1e6, 1),
+            "workload": "mixed iteration (240 decode seqs, 16 prefill chunks x 512), "
+                        "pool after its append"}
 
 
 def kernel_source_hash() -> str:
@@ -696,6 +750,11 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+
+    if args.loop:
+        print(json.dumps(loop_calls(pa, torch, make_workload, args.loop, args.loop_seconds)),
+              flush=True)
+        return 0
 
     if args.rows_only:
         result = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1,
