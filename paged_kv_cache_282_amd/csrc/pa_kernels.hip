@@ -14,9 +14,11 @@
 //   * Decode works on items (sequence, kv head, 1024-token partition) that a
 //     persistent grid takes from a queue; a workgroup's four waves take
 //     interleaved 32-token steps of an item, keep an online softmax state
-//     each and merge in LDS. A sequence of several partitions publishes one
-//     partial per partition, and a second kernel merges them (log-sum-exp
-//     identity). The grid size and the loads' cache policy follow the batch.
+//     each and merge in LDS. A sequence of several partitions gets one
+//     partial per partition, which the persistent kernel folds into the
+//     sequence's output itself (log-sum-exp identity); only the fallback for
+//     batches of more than 2048 sequences leaves them to a second kernel. The
+//     grid size and the loads' cache policy follow the batch.
 //   * bf16 decode: scores and p.V run on v_mfma_f32_16x16x32_bf16, whose 16
 //     columns are the query heads of one GQA group (padded); bf16 prefill runs
 //     on v_mfma_f32_32x32x16_bf16, whose 32 columns are (position, head) rows.
@@ -158,7 +160,8 @@ __device__ __forceinline__ int clamp_block(int blk, int64_t nb) {
 
 // ---------------------------------------------------------------------------
 // bf16 decode MFMA engine: online-softmax attention of NT column tiles of 16
-// query rows over 32-token steps of one kv head.
+// query rows over 32-token steps of one kv head (every kernel here uses one
+// tile, NT = 1).
 //
 // A step is 32 tokens: set a = tokens 0..15, set b = tokens 16..31 (two
 // blocks of 16, or the two halves of one block of 32).
