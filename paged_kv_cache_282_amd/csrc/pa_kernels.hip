@@ -1321,7 +1321,10 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
     if constexpr (SH) {
       if (it.p == it.S && it.S > 0) {
         // a stacked member's first own partition: its shared partitions'
-        // partials first, as stored, in partition order
+        // partials first, as stored, in partition order (other waves of this
+        // workgroup stored them while an earlier item ran; that item's closing
+        // __syncthreads, a workgroup-scope release and acquire, orders those
+        // stores before these loads)
         ms.reset();
         for (int p2 = 0; p2 < it.S; ++p2) {
           const int64_t at = partial_at(it.b, it.g, row, p2);
