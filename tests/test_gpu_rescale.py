@@ -17,9 +17,10 @@ scores (base-2 units, x = q.k * scale * log2 e) along one key dimension:
 
 Every pattern runs at a short and a long length (the long one spans two
 decode partitions), through the decode, the prefill and the single-launch
-mixed batch, at block sizes 16 and 32. Outputs are checked against the fp64
-oracle under the bfloat16 rounding bound of test_gpu_discriminating.py, and
-the mixed launch must equal the separate calls bit for bit.
+mixed batch, at block sizes 16 and 32 (head dim 128) and at head dim 64.
+Outputs are checked against the fp64 oracle under the bfloat16 rounding bound
+of test_gpu_discriminating.py, and the mixed launch must equal the separate
+calls bit for bit.
 """
 import numpy as np
 import pytest
@@ -33,8 +34,7 @@ from workloads import f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
-HKV, HQ, D = 2, 8, 128
-SCALE = 1.0 / np.sqrt(D)
+HKV, HQ = 2, 8
 BETA = 16.0  # query component along the steering dimension (bf16-exact)
 LENGTHS = (300, 1100)
 PATTERNS = ("ramp", "plateau", "jump", "fall")
@@ -62,9 +62,10 @@ def _bf16_values(x):
     return (f32_to_bf16_bits(np.asarray(x, np.float32)).astype(np.uint32) << 16).view(np.float32)
 
 
-def _inputs(seed):
+def _inputs(seed, D):
     rng = np.random.default_rng(seed)
-    per_unit = BETA * float(np.float32(SCALE)) * np.log2(np.e)  # x per unit of the key component
+    scale = 1.0 / np.sqrt(D)
+    per_unit = BETA * float(np.float32(scale)) * np.log2(np.e)  # x per unit of the key component
     K, V, lens = [], [], []
     for length in LENGTHS:
         for pattern in PATTERNS:
@@ -76,7 +77,7 @@ def _inputs(seed):
     return K, V, np.array(lens, np.int32), rng
 
 
-def _queries(rng, rows):
+def _queries(rng, rows, D):
     q = rng.normal(0.0, 0.05, (rows, HQ, D))
     q[:, :, 0] = BETA
     return f32_to_bf16_bits(q.astype(np.float32))
@@ -97,17 +98,18 @@ def _check_bound(got, o, ma, md, label):
     assert (err <= bound).all(), f"{int((err > bound).sum())} elements exceed the bound"
 
 
-@pytest.mark.parametrize("bs", [16, 32])
-def test_rescale_patterns_within_the_rounding_bound(bs):
-    K, V, lens, rng = _inputs(900 + bs)
+@pytest.mark.parametrize("bs,D", [(16, 128), (32, 128), (16, 64)])
+def test_rescale_patterns_within_the_rounding_bound(bs, D):
+    scale = 1.0 / np.sqrt(D)
+    K, V, lens, rng = _inputs(900 + bs + D, D)
     pool_f, tables = contiguous_pool(K, V, bs, np.float32)
     pool = f32_to_bf16_bits(pool_f.astype(np.float32))  # the pad block's NaN stays NaN
     B = len(lens)
     max_len = int(lens.max())
-    qd = _queries(rng, B)
+    qd = _queries(rng, B, D)
     Lc = np.minimum(lens, 256)
     qsl = np.concatenate([[0], np.cumsum(Lc)]).astype(np.int32)
-    qp = _queries(rng, int(qsl[-1]))
+    qp = _queries(rng, int(qsl[-1]), D)
     _say(f"[case] rescale patterns bs={bs}: B={B} Hq={HQ} Hkv={HKV} d={D} "
          f"lens={sorted(set(lens.tolist()))} prefill rows={int(qsl[-1])}")
 
@@ -117,16 +119,16 @@ def test_rescale_patterns_within_the_rounding_bound(bs):
     ws = pa.new_decode_workspace(B, HQ, D, max_len)
     out = torch.empty_like(qd_d)
     pout = torch.empty_like(qp_d)
-    pa.pa_decode(out, qd_d, pool_d, tab_d, len_d, max_len, HKV, bs, SCALE, ws)
-    pa.pa_prefill_chunk(pout, qp_d, pool_d, tab_d, len_d, qsl_d, int(Lc.max()), HKV, bs, SCALE)
+    pa.pa_decode(out, qd_d, pool_d, tab_d, len_d, max_len, HKV, bs, scale, ws)
+    pa.pa_prefill_chunk(pout, qp_d, pool_d, tab_d, len_d, qsl_d, int(Lc.max()), HKV, bs, scale)
     out2, pout2 = torch.empty_like(out), torch.empty_like(pout)
     pa.pa_mixed_attention(out2, qd_d, tab_d, len_d, max_len, pout2, qp_d, tab_d, len_d, qsl_d,
-                          int(Lc.max()), pool_d, HKV, bs, SCALE, ws)
+                          int(Lc.max()), pool_d, HKV, bs, scale, ws)
     torch.cuda.synchronize()
 
-    o, ma, md = oracle.decode_moments(qd, pool, tables, lens, HKV, bs, SCALE, "bf16")
+    o, ma, md = oracle.decode_moments(qd, pool, tables, lens, HKV, bs, scale, "bf16")
     _check_bound(values(out), o, ma, md, "decode")
-    o, ma, md = oracle.prefill_moments(qp, pool, tables, lens, qsl, HKV, bs, SCALE, "bf16")
+    o, ma, md = oracle.prefill_moments(qp, pool, tables, lens, qsl, HKV, bs, scale, "bf16")
     _check_bound(values(pout), o, ma, md, "prefill")
     assert np.array_equal(bits(out2), bits(out)), "mixed launch decode differs from pa_decode"
     assert np.array_equal(bits(pout2), bits(pout)), "mixed launch prefill differs from pa_prefill_chunk"
