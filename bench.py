@@ -18,8 +18,8 @@ Reported (one JSON line on stdout):
              (each attended token's K and V read once per (sequence, kv head))
   roofline   pa_decode on the headline batch: algorithmic bytes per call / its
              mean duration (HIP events on the launch stream around graph
-             replays of back-to-back calls over the layer pools; a call runs
-             the partition kernel and the split-K merge kernel), against
+             replays of back-to-back calls over the layer pools; a call is one
+             persistent kernel, which folds its split-K partitions itself), against
              8 TB/s and against a measured streaming rate (one pa_copy_blocks
              call of about 1.7 GB read + written); `traffic` is the HBM bytes
              per call measured with rocprofv3 counters for this exact kernel
@@ -38,6 +38,10 @@ Reported (one JSON line on stdout):
              kernels on a long-tail request stream, under paged allocation,
              Orca-style max-length reservation and static batching: output
              tokens/s, host time per iteration, decode KV GB/s of the loop
+
+With --loop decode|prefill|mixed it measures nothing: it runs that call of the
+mixed iteration back to back for --loop-seconds, a steady load for sampling
+board power and clocks from outside (amd-smi), and prints calls and time.
 """
 from __future__ import annotations
 
