@@ -156,7 +156,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  *                 stream; calls that may run concurrently need separate
  *                 workspaces.
  * Sequences longer than PA_DECODE_PARTITION are split into partitions whose
- * partial softmax states are merged by a second kernel on the same stream.
+ * partial softmax states are merged in partition order: inside the same
+ * kernel for bfloat16 batches of up to 2048 sequences, by a second kernel on
+ * the same stream otherwise.
  * Cache behaviour: a call whose K+V exceeds 256 MiB and in which no sequence
  * starts with its predecessor's first block streams K/V with nontemporal
  * loads (they are not kept in the caches); other calls load them cached. The
