@@ -761,6 +761,7 @@ struct ScanSmem {
   // member count - 1 (bits 11..14) and its shared partitions (bits 16..31).
   int order[kMaxScanSeqs];
   int wsum[kOrderClasses / 4 + 1][kWaves][2];  // one scratch row per block scan
+  int ccount[kWaves][kOrderClasses];           // units per wave and class (one sequence per thread)
   unsigned long long tokens;  // sum of the clamped context lengths
   int shared;                 // some sequence starts with its predecessor's first block
   int units;                  // number of units per kv head
@@ -793,24 +794,22 @@ __device__ __forceinline__ int order_class(int n) {
   return np >= 2 ? min(kOrderClasses - 1, 7 + np) : min(7, n / (kPartition / 8));
 }
 
-// Exclusive block-wide maximum (256 threads, -1 before thread 0); scratch is
-// one row of ScanSmem::wsum, which no other scan of the same call uses.
-__device__ __forceinline__ int block_max_excl(int (&wsum)[kWaves][2], int x) {
+// Exclusive block-wide maximum (256 threads, -1 before thread 0) of values x
+// that are -1 or grow with the thread index: the nearest lower thread's x that
+// is not -1. Scratch is one row of ScanSmem::wsum, which no other scan of the
+// same call uses.
+__device__ __forceinline__ int block_last_excl(int (&wsum)[kWaves][2], int x) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int ix = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(ix, d);
-    if (lane >= d) ix = max(ix, o);
-  }
-  if (lane == 63) wsum[wave][0] = ix;
+  const uint64_t m = __builtin_amdgcn_ballot_w64(x >= 0);
+  if (lane == 0) wsum[wave][0] = m != 0 ? __builtin_amdgcn_readlane(x, 63 - __builtin_clzll(m)) : -1;
+  const uint64_t below = m & ((1ull << lane) - 1);
+  const int inw = __shfl(x, below != 0 ? 63 - __builtin_clzll(below) : 0);
   __syncthreads();
   int b = -1;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w)
     if (w < wave) b = max(b, wsum[w][0]);
-  const int before = __shfl_up(ix, 1);
-  return max(b, lane > 0 ? before : -1);
+  return below != 0 ? inw : b;
 }
 
 // Exclusive block-wide scan (256 threads) of a pair of counts; scratch is one
@@ -997,7 +996,7 @@ __device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __rest
       const int i = threadIdx.x * per + c;
       if (c < per && i < B && link(i) == 0) last_start = i;
     }
-    int run = block_max_excl(sc.wsum[kOrderClasses / 4], last_start);
+    int run = block_last_excl(sc.wsum[kOrderClasses / 4], last_start);
     const int G = a.hq / a.hkv;
     const int gmax = max(1, kStackRows / G);
 #pragma unroll
@@ -1030,47 +1029,85 @@ __device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __rest
       }
     }
   }
-  // Count this thread's units per class, two 16-bit counts per word (a
-  // count never exceeds kMaxScanSeqs < 2^16), and scan the counts over the
-  // block: each class's start in the order, and this thread's offset in it.
-  int cnt[kOrderClasses / 2];
-#pragma unroll
-  for (int k = 0; k < kOrderClasses / 2; ++k) cnt[k] = 0;
-#pragma unroll
-  for (int c = 0; c < kPer; ++c)
-    if (cls[c] >= 0) cnt[cls[c] >> 1] += 1 << (16 * (cls[c] & 1));
+  // Rank the units: by class, largest first, and by sequence index within a
+  // class. pos[c] is unit c's place in the order.
   if (threadIdx.x == 0) {
     sc.tokens = 0;
     sc.shared = 0;
   }
-  int ex[kOrderClasses / 2], tot[kOrderClasses / 2];
+  int pos[kPer];
 #pragma unroll
-  for (int k = 0; k < kOrderClasses / 2; k += 2)  // (the first barrier also orders the clears)
-    block_scan2(sc.wsum[k / 2], cnt[k], cnt[k + 1], ex[k], ex[k + 1], tot[k], tot[k + 1]);
-  if (tok != 0) atomicAdd(&sc.tokens, static_cast<unsigned long long>(tok));
-  if (shared) atomicOr(&sc.shared, 1);
-  // class starts, largest class first
-  int start[kOrderClasses];
-  int run = 0;
+  for (int c = 0; c < kPer; ++c) pos[c] = 0;
+  if (per == 1) {
+    // One sequence per thread: a ballot per class gives each unit its rank
+    // among the units of its class in lower lanes, and each wave's count.
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int rank = 0, wc = 0;
 #pragma unroll
-  for (int k = kOrderClasses - 1; k >= 0; --k) {
-    start[k] = run;
-    run += (tot[k >> 1] >> (16 * (k & 1))) & 0xFFFF;
-  }
-  if (threadIdx.x == 0) sc.units = run;
+    for (int k = 0; k < kOrderClasses; ++k) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(cls[0] == k);
+      if (cls[0] == k)
+        rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                         __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+      if (lane == k) wc = __builtin_popcountll(m);
+    }
+    if (lane < kOrderClasses) sc.ccount[wave][lane] = wc;
+    __syncthreads();  // (also orders the clears above)
+    // the unit's place: the units of every larger class, then those of its
+    // class in lower waves, then in lower lanes
+    int units = 0;
+    pos[0] = rank;
 #pragma unroll
-  for (int c = 0; c < kPer; ++c) {
-    const int i = threadIdx.x * per + c;
-    if (cls[c] >= 0) {
-      int pos = 0, before_here = 0;
+    for (int k = kOrderClasses - 1; k >= 0; --k) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int c = sc.ccount[w][k];
+        units += c;
+        pos[0] += (k > cls[0] || (k == cls[0] && w < wave)) ? c : 0;
+      }
+    }
+    if (threadIdx.x == 0) sc.units = units;
+  } else {
+    // Count this thread's units per class, two 16-bit counts per word (a
+    // count never exceeds kMaxScanSeqs < 2^16), and scan the counts over the
+    // block: each class's start in the order, and this thread's offset in it.
+    int cnt[kOrderClasses / 2];
+#pragma unroll
+    for (int k = 0; k < kOrderClasses / 2; ++k) cnt[k] = 0;
+#pragma unroll
+    for (int c = 0; c < kPer; ++c)
+      if (cls[c] >= 0) cnt[cls[c] >> 1] += 1 << (16 * (cls[c] & 1));
+    int ex[kOrderClasses / 2], tot[kOrderClasses / 2];
+#pragma unroll
+    for (int k = 0; k < kOrderClasses / 2; k += 2)  // (the first barrier also orders the clears)
+      block_scan2(sc.wsum[k / 2], cnt[k], cnt[k + 1], ex[k], ex[k + 1], tot[k], tot[k + 1]);
+    // class starts, largest class first
+    int start[kOrderClasses];
+    int run = 0;
+#pragma unroll
+    for (int k = kOrderClasses - 1; k >= 0; --k) {
+      start[k] = run;
+      run += (tot[k >> 1] >> (16 * (k & 1))) & 0xFFFF;
+    }
+    if (threadIdx.x == 0) sc.units = run;
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      int p = 0, before_here = 0;
 #pragma unroll
       for (int k = 0; k < kOrderClasses; ++k)
-        if (k == cls[c]) pos = start[k] + ((ex[k >> 1] >> (16 * (k & 1))) & 0xFFFF);
+        if (k == cls[c]) p = start[k] + ((ex[k >> 1] >> (16 * (k & 1))) & 0xFFFF);
 #pragma unroll
       for (int c2 = 0; c2 < kPer; ++c2)
         before_here += (c2 < c && cls[c2] == cls[c]) ? 1 : 0;
-      sc.order[pos + before_here] = val[c];
+      pos[c] = p + before_here;
     }
+  }
+  if (tok != 0) atomicAdd(&sc.tokens, static_cast<unsigned long long>(tok));
+  if (shared) atomicOr(&sc.shared, 1);
+#pragma unroll
+  for (int c = 0; c < kPer; ++c) {
+    const int i = threadIdx.x * per + c;
+    if (cls[c] >= 0) sc.order[pos[c]] = val[c];
     if (c < per && i < B) sc.n[i] = nl[c];
   }
   __syncthreads();
