@@ -850,6 +850,25 @@ def main() -> int:
     decode_ms, append_ms = dec[0], app[0]
     dec_p10, dec_p90 = dec[1], dec[2]
 
+    # The same step with each layer's append and decode in one call
+    # (pa_decode_append, bit-identical outputs and pool): the whole step as a
+    # graph, and one call, both timed like the rows above. Reported beside the
+    # headline, which keeps the two calls of the step as the pages describe it.
+    def fused_step():
+        for l in range(L):
+            pa.pa_decode_append(outs[l], q, pools[l], tables, lens, k_new, v_new, slots, max_ctx,
+                                hkv, bs, scale, ws)
+
+    def fused_next():
+        l = k[0] % L
+        pa.pa_decode_append(outs[l], q, pools[l], tables, lens, k_new, v_new, slots, max_ctx,
+                            hkv, bs, scale, ws)
+        k[0] += 1
+
+    fstep = time_calls(fused_step, torch, 2)
+    fcall = time_calls(fused_next, torch, 4 * L)
+    split_step = time_calls(step, torch, 2)
+
     # A measured streaming rate beside the vendor figure: one pa_copy_blocks
     # call copying half of the first layer's pool onto its other half (pairs
     # (j, half + j): disjoint, inside the pool), far more than the 256 MB
@@ -889,6 +908,14 @@ def main() -> int:
                    "kv_bytes_per_layer": int(kv_bytes_layer)},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_layers_per_s": round(w.num_seqs * L / (ms_per_step * 1e-3), 1),
+        "fused_step": {"entry": "pa_decode_append (per layer: the append and the decode in one "
+                                "launch; outputs and pool bit-identical to the two calls)",
+                       "ms_per_step": round(fstep[0], 4),
+                       "split_ms_per_step": round(split_step[0], 4),
+                       "timing": "per step, median of graph replays of two back-to-back steps; "
+                                 "both forms in the same run",
+                       "pa_decode_append_ms": round(fcall[0], 4),
+                       "value": round(kv_bytes(w) * L / (fstep[0] * 1e-3) / 1e9, 2)},
         "kernels_ms": {"pa_decode": round(decode_ms, 4),
                        "pa_decode_p10": round(dec_p10, 4),
                        "pa_decode_p90": round(dec_p90, 4),

@@ -198,6 +198,36 @@ int pa_decode_shared(void* out, const void* q, const void* kv_pool, const int32_
                      size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_append — one decode step: each sequence's new token is appended,
+ * then every sequence attends over its context including that token.
+ * ("Paging the KV Cache", "The waste hiding inside memory": the cache grows by
+ * one token per generated token; worksonmygpu.com continuous-batching post,
+ * "Selective batching": each request's attention over its own tokens.)
+ *
+ * The same results as pa_append_kv(kv_pool, k_new, v_new, slot_mapping,
+ * num_seqs, ...) followed by pa_decode(...) on the same stream, bit for bit,
+ * for calls in which slot_mapping[b] is the pool slot of position
+ * context_lens[b]-1 in sequence b's table (as a scheduler's append gives).
+ * Arguments as pa_decode, plus
+ *   k_new, v_new  [num_seqs][num_kv_heads][head_dim], 16-byte aligned: the
+ *                 key and value of position context_lens[b]-1 of sequence b.
+ *   slot_mapping  [num_seqs] int32: the pool slot they are written to
+ *                 (negative: not written; the attention still uses them).
+ * The pool holds every new token when the call's work completes, as after
+ * pa_append_kv; the call's own attention takes the new tokens from k_new and
+ * v_new, not from the pool. bfloat16 batches of at most 2048 sequences run as
+ * one kernel, which writes the new tokens after its loads; other calls run
+ * the append and then the decode. Errors as pa_decode, and PA_ERR_NULL /
+ * PA_ERR_ALIGN for k_new, v_new or slot_mapping.
+ */
+int pa_decode_append(void* out, const void* q, void* kv_pool, const int32_t* block_tables,
+                     const int32_t* context_lens, const void* k_new, const void* v_new,
+                     const int32_t* slot_mapping, int32_t num_seqs, int32_t max_blocks_per_seq,
+                     int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                     int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill_chunk — attention of prefill chunks over a paged cache.
  * (worksonmygpu.com continuous-batching post, "The prefill/decode mix":
  * prompt chunks share the iteration with decode steps.)

@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = ["PAError", "load", "lib_path", "pa_append_kv", "pa_copy_blocks", "pa_decode",
-           "pa_decode_workspace_size", "pa_decode_noalloc", "pa_decode_shared", "pa_prefill_chunk",
+           "pa_decode_workspace_size", "pa_decode_noalloc", "pa_decode_shared", "pa_decode_append",
+           "pa_prefill_chunk",
            "pa_mixed_attention",
            "pa_swap_blocks", "SWAP_OUT", "SWAP_IN",
            "pa_status_string", "new_decode_workspace", "DECODE_PARTITION"]
@@ -76,6 +77,11 @@ def load() -> ctypes.CDLL:
                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      ctypes.c_float, _c_int, _c_ptr, ctypes.c_size_t, _c_ptr]
     lib.pa_decode_shared.restype = ctypes.c_int
+    lib.pa_decode_append.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                     _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     _c_int, _c_int, ctypes.c_float, _c_int, _c_ptr,
+                                     ctypes.c_size_t, _c_ptr]
+    lib.pa_decode_append.restype = ctypes.c_int
     lib.pa_prefill_chunk.argtypes = [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int,
                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_int, ctypes.c_float, _c_int, _c_ptr]
@@ -240,6 +246,33 @@ def pa_decode_shared(out, q, kv_pool, block_tables, context_lens, share_prev,
         _i32(block_tables, "block_tables"), _i32(context_lens, "context_lens"), share, B, mb,
         int(max_context_len), hq, num_kv_heads, d, block_size, nb, float(scale),
         _dtype_code(q, kv_pool, out), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def pa_decode_append(out, q, kv_pool, block_tables, context_lens, k_new, v_new, slot_mapping,
+                     max_context_len: int, num_kv_heads: int, block_size: int, scale: float,
+                     workspace, stream=None):
+    """One decode step: append k_new / v_new [B][Hkv][d] (position context_lens[b]-1
+    of sequence b) at ``slot_mapping`` [B], then pa_decode over contexts that include
+    them. Same results as pa_append_kv followed by pa_decode. Fills ``out`` and
+    returns it."""
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B][Hq][d], got {tuple(q.shape)}")
+    B, hq, d = q.shape
+    _expect(out, (B, hq, d), "out")
+    _expect(context_lens, (B,), "context_lens")
+    _expect(k_new, (B, num_kv_heads, d), "k_new")
+    _expect(v_new, (B, num_kv_heads, d), "v_new")
+    _expect(slot_mapping, (B,), "slot_mapping")
+    mb = _rows(block_tables, B, "block_tables")
+    nb = _num_blocks(kv_pool, num_kv_heads, block_size, d)
+    _check("pa_decode_append", load().pa_decode_append(
+        _dev(out, "out"), _dev(q, "q"), _dev(kv_pool, "kv_pool"),
+        _i32(block_tables, "block_tables"), _i32(context_lens, "context_lens"),
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _i32(slot_mapping, "slot_mapping"), B, mb,
+        int(max_context_len), hq, num_kv_heads, d, block_size, nb, float(scale),
+        _dtype_code(q, kv_pool, out, k_new, v_new), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 

@@ -199,6 +199,30 @@ int pa_decode_shared(void* out, const void* q, const void* kv_pool, const int32_
                                      share_prev));
 }
 
+int pa_decode_append(void* out, const void* q, void* kv_pool, const int32_t* block_tables,
+                     const int32_t* context_lens, const void* k_new, const void* v_new,
+                     const int32_t* slot_mapping, int32_t num_seqs, int32_t max_blocks_per_seq,
+                     int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                     int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || max_context_len < 0) return PA_ERR_SHAPE;
+  if (int s = check_pool(num_blocks, num_kv_heads, head_dim, block_size, dtype)) return s;
+  if (int s = check_heads(num_q_heads, num_kv_heads)) return s;
+  if (num_seqs == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return PA_ERR_ALIGN;
+  if (int64_t(num_blocks) * block_size > INT32_MAX) return PA_ERR_SHAPE;
+  if (int s = check_decode(out, q, kv_pool, block_tables, context_lens, num_seqs,
+                           max_blocks_per_seq, max_context_len, num_q_heads, num_kv_heads,
+                           head_dim, block_size, dtype, workspace, workspace_bytes))
+    return s;
+  return status_of(pa::launch_decode_append(
+      out, q, kv_pool, block_tables, context_lens, k_new, v_new, slot_mapping, num_seqs,
+      max_blocks_per_seq, max_context_len, num_q_heads,
+      shape(num_blocks, num_kv_heads, head_dim, block_size), scale, dtype, workspace,
+      static_cast<hipStream_t>(stream)));
+}
+
 int pa_decode_noalloc(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
                       const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                       int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,

@@ -639,6 +639,12 @@ struct DecodeArgs {
   // Caller's sharing hint (nullptr: none): share[b] leading tokens of sequence
   // b are said to live in the same blocks as sequence b-1's.
   const int32_t* share;
+  // Decode step with its append (nullptr: none): k_new / v_new
+  // [num_seqs][hkv][D] are the keys and values at position lens[b]-1 of
+  // sequence b, written to pool slot slots[b] (negative: not written).
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slots;
 };
 
 // Resolves (sequence, kv head, partition) of this workgroup; false if idle.
@@ -1143,7 +1149,14 @@ __device__ __forceinline__ bool decode_scan(const DecodeArgs& a, int32_t* __rest
 // HANDOVER: a wave hands over to the next item as soon as its own steps of the
 // current one are done (below); this needs more registers than two
 // workgroups per compute unit leave, so the mixed launch runs without it.
-template <int D, int BS, int POL, bool SH = false, int R = kMaxGroup, bool HANDOVER = false>
+//
+// FUSED: each sequence's new token (k_new, v_new) is its key and value at
+// position lens[b]-1. The wave whose step reads that position replaces the
+// token's K and V in the step's registers with them, which is what the step
+// would have loaded had the token been appended first; the pool itself is
+// written by the kernel itself (append_load, append_store).
+template <int D, int BS, int POL, bool SH = false, int R = kMaxGroup, bool HANDOVER = false,
+          bool FUSED = false>
 __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __restrict__ queue,
                                             DecodeSmem<D, R>& ds, int rank, int dealt) {
   using Eng = Bf16Engine<D, BS, 1>;
@@ -1179,6 +1192,12 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
     // SH, shared items: lane l's entry of member 4k + l/16, for the check
     int entm[kStackRows / 4];
     bool ok;  // SH: this wave's block ids are every member's
+    // FUSED: the new token's position (-1: not in this item), K slice
+    // lane % (D/8) of its row and V dimensions 2 lane, 2 lane + 1 (the patch
+    // gathers each lane's parts from these with lane shuffles)
+    int pn;
+    u32x4 knew;
+    uint32_t vnew;
   };
   // rows of MFMA columns an item's results occupy
   auto rows_of = [&](const QItem& it) { return (SH && it.stacked) ? it.ucnt * G : G; };
@@ -1214,6 +1233,16 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
     }
     make_uniform(pl.it);
     if constexpr (SH) make_uniform_stack(pl.it);
+    if constexpr (FUSED) {
+      pl.pn = (pl.it.unit < total && pl.it.p == pl.it.np - 1 && pl.it.tok1 > pl.it.tok0)
+                  ? pl.it.tok1 - 1
+                  : -1;
+      const int64_t row = (static_cast<int64_t>(pl.it.b) * a.hkv + pl.it.g) * D;
+      const auto kr = tile_rsrc(static_cast<const uint16_t*>(a.k_new) + row, pl.pn >= 0 ? D * 2 : 0);
+      const auto vr = tile_rsrc(static_cast<const uint16_t*>(a.v_new) + row, pl.pn >= 0 ? D * 2 : 0);
+      pl.knew = __builtin_amdgcn_raw_buffer_load_b128(kr, (lane & (D / 8 - 1)) * 16, 0, kCached);
+      pl.vnew = __builtin_amdgcn_raw_buffer_load_b32(vr, lane * 4, 0, kCached);  // D 64: lanes < 32
+    }
     const int32_t* trow = a.tables + static_cast<int64_t>(pl.it.b) * a.mb;
     const int l = lane < 2 * kSteps ? lane : 0;
     const int base =
@@ -1301,6 +1330,46 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
   auto issue = [&](const Plan& pl, int s2, typename Eng::KV& buf) {
     issue_ids(pl.it.g, pl.idA[s2], pl.idB[s2],
               pl.it.tok0 + kStep * (wave + kWaves * s2) < pl.it.tok1, buf);
+  };
+  // FUSED: in the step starting at t0 that holds the new token, its K (the
+  // lanes of its token row r, set a or b) and its V (the lanes of its 4-token
+  // slice, one 16-bit half of one word) become the token's own.
+  auto patch = [&](typename Eng::KV& kv, int t0, const Plan& pl) {
+    if constexpr (FUSED) {
+      if (t0 <= pl.pn && pl.pn < t0 + kStep) {  // wave-uniform
+        const int tl = pl.pn - t0, t16 = tl & 15;
+        const bool setb = tl >= 16;
+        // (each field written unconditionally: one store through a pointer
+        // chosen between kA and kB would keep the step in scratch memory too)
+        const bool ka = r == t16 && !setb, kb = r == t16 && setb;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+          u32x4 k;  // slice kg + 4 s2
+#pragma unroll
+          for (int x = 0; x < 4; ++x) k[x] = __shfl(pl.knew[x], kg + 4 * s2);
+          kv.kA[s2] = ka ? k : kv.kA[s2];
+          kv.kB[s2] = kb ? k : kv.kB[s2];
+        }
+        // word w = 2 (set b) + (t16 % 4) / 2 of the lanes of slice t16 / 4,
+        // 16-bit half t16 % 2; the per-word masks are plain arithmetic, so
+        // that no word is picked by a run-time index (which would move the
+        // step's registers to scratch memory)
+        const int w = (setb ? 2 : 0) + ((t16 & 3) >> 1);
+        const int sh = 16 * (t16 & 1);
+        const uint32_t sel = kg == (t16 >> 2) ? 1u << w : 0u;
+        uint32_t msk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) msk[e] = (0u - ((sel >> e) & 1u)) & (0xFFFFu << sh);
+#pragma unroll
+        for (int j = 0; j < Eng::VT; ++j) {
+          // dimension r + 16 j: half r % 2 of lane (r + 16 j) / 2's pair
+          const uint32_t d2 = __shfl(pl.vnew, (r + 16 * j) >> 1);
+          const uint32_t v = ((d2 >> (16 * (r & 1))) & 0xFFFFu) << sh;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kv.vv[j][e] = (kv.vv[j][e] & ~msk[e]) | (v & msk[e]);
+        }
+      }
+    }
   };
 
   // The wave states of item i are combined and folded while item i+1's steps
@@ -1432,7 +1501,10 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
 #pragma unroll
     for (int s2 = 0; s2 < kSteps; ++s2) {
       const int t0 = cur.it.tok0 + kStep * (wave + kWaves * s2);
-      if (t0 < cur.it.tok1) eng.compute(kv[s2 & 1], t0, cur.it.tok1, lane, a.sl2e);
+      if (t0 < cur.it.tok1) {
+        patch(kv[s2 & 1], t0, cur);
+        eng.compute(kv[s2 & 1], t0, cur.it.tok1, lane, a.sl2e);
+      }
       if (s2 == kSteps - 2 && new_unit && threadIdx.x == 0) {
         // Take the unit after next; the id goes to LDS just before the
         // barrier, when waiting for it no longer holds back any load.
@@ -1474,7 +1546,10 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
     auto step_and_issue = [&](auto sc, bool last) {
       constexpr int s = decltype(sc)::value;
       const int t0 = cur.it.tok0 + kStep * (wave + kWaves * s);
-      if (t0 < cur.it.tok1) eng.compute(kv[s & 1], t0, cur.it.tok1, lane, a.sl2e);
+      if (t0 < cur.it.tok1) {
+        patch(kv[s & 1], t0, cur);
+        eng.compute(kv[s & 1], t0, cur.it.tok1, lane, a.sl2e);
+      }
       if ((s & 1) == 0 && last) hand_over();
       const int idA = last ? nxt.idA[s & 1] : (s + 2 < kSteps ? cur.idA[(s + 2) % kSteps] : 0);
       const int idB = last ? nxt.idB[s & 1] : (s + 2 < kSteps ? cur.idB[(s + 2) % kSteps] : 0);
@@ -1541,7 +1616,8 @@ __device__ __forceinline__ void decode_loop(const DecodeArgs& a, int32_t* __rest
 // The whole decode of one workgroup: scan, then the loop under the call's
 // cache policy (the same in every workgroup: it depends only on the inputs).
 // rank, dealt: see decode_loop.
-template <int D, int BS, bool SH = false, int R = kMaxGroup, bool HANDOVER = false>
+template <int D, int BS, bool SH = false, int R = kMaxGroup, bool HANDOVER = false,
+          bool FUSED = false>
 __device__ __forceinline__ void decode_persistent(const DecodeArgs& a, int32_t* __restrict__ queue,
                                                   DecodeSmem<D, R>& ds, int rank, int dealt) {
   // The hand-over pays where loads return quickly and items are short
@@ -1550,9 +1626,9 @@ __device__ __forceinline__ void decode_persistent(const DecodeArgs& a, int32_t* 
   // branches make the loads wait more (measured 226 -> 237 us on the GQA
   // long-tail batch), while it gains 124 -> 106 us on the shared-prefix batch.
   if (decode_scan<D, BS, SH>(a, queue, ds))
-    decode_loop<D, BS, kCached, SH, R, HANDOVER>(a, queue, ds, rank, dealt);
+    decode_loop<D, BS, kCached, SH, R, HANDOVER, FUSED>(a, queue, ds, rank, dealt);
   else
-    decode_loop<D, BS, kNontemporal, SH, R, false>(a, queue, ds, rank, dealt);
+    decode_loop<D, BS, kNontemporal, SH, R, false, FUSED>(a, queue, ds, rank, dealt);
 }
 
 // (launched one workgroup per compute unit: see launch_decode_bf16)
@@ -1572,6 +1648,93 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_bf16_shared_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
   __shared__ DecodeSmem<D, kStackRows> ds;
   decode_persistent<D, BS, true, kStackRows, true>(a, queue, ds, blockIdx.x, gridDim.x);
+  leave_queue(queue);
+}
+
+// The append of a fused decode step: every (sequence, kv head)'s new token
+// goes to its slot. No read of this call needs the slot's contents (the wave
+// whose step holds the position uses k_new / v_new instead, and a slot being
+// appended to belongs to its sequence alone), so the stores may land at any
+// time. Workgroup w takes pairs w, w + W, ... (W workgroups), wave v of them
+// every fourth. The first kAppendRound pairs of each wave are loaded before
+// the scan, in its round trip, and stored after the loop, when no wait of the
+// wave's loads can be held back by them (stored right after the scan instead,
+// they made the step 4.6% slower); any further pairs (over kAppendRound * 4 * W
+// of them) are loaded and stored after the loop.
+constexpr int kAppendRound = 2;
+template <int D>
+struct AppendRound {
+  u32x4 k[kAppendRound];     // lane < D/8: K slice `lane`
+  uint32_t v[kAppendRound];  // V dimensions 2 lane, 2 lane + 1 (D 64: lanes < 32)
+  int slot[kAppendRound];    // wave-uniform; -1: nothing to write
+  int pr[kAppendRound];
+};
+template <int D, int BS>
+__device__ __forceinline__ void append_load(const DecodeArgs& a, AppendRound<D>& ar, int first) {
+  const int pairs = a.num_seqs * a.hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int stride = static_cast<int>(gridDim.x) * kWaves;
+#pragma unroll
+  for (int k = 0; k < kAppendRound; ++k) {
+    const int pr = first + (static_cast<int>(blockIdx.x) * kWaves + wave) + k * stride;
+    const bool in = pr < pairs;
+    const int b = in ? pr / a.hkv : 0;
+    const int64_t src = (static_cast<int64_t>(in ? pr : 0)) * D;
+    const auto kr = tile_rsrc(static_cast<const uint16_t*>(a.k_new) + src, in ? D * 2 : 0);
+    const auto vr = tile_rsrc(static_cast<const uint16_t*>(a.v_new) + src, in ? D * 2 : 0);
+    ar.k[k] = __builtin_amdgcn_raw_buffer_load_b128(kr, (lane & (D / 8 - 1)) * 16, 0, kCached);
+    ar.v[k] = __builtin_amdgcn_raw_buffer_load_b32(vr, lane * 4, 0, kCached);
+    ar.slot[k] = in ? a.slots[b] : -1;
+    ar.pr[k] = pr;
+  }
+}
+template <int D, int BS>
+__device__ __forceinline__ void append_store(const DecodeArgs& a, const AppendRound<D>& ar) {
+  const int lane = threadIdx.x & 63;
+  uint16_t* pool = static_cast<uint16_t*>(const_cast<void*>(a.pool));
+#pragma unroll
+  for (int k = 0; k < kAppendRound; ++k) {
+    const int slot = __builtin_amdgcn_readfirstlane(ar.slot[k]);
+    if (slot < 0 || static_cast<int64_t>(slot) >= a.nb * BS) continue;  // wave-uniform
+    const int g = ar.pr[k] - (ar.pr[k] / a.hkv) * a.hkv;
+    const int64_t blk = slot / BS;
+    const int off = slot - static_cast<int>(blk) * BS;
+    uint16_t* base = pool + blk * a.blk_elems;
+    // K: lane < D/8 writes 8-element slice `lane` at the slot
+    if (lane < D / 8)
+      st16(base + static_cast<int64_t>(g) * BS * D + (static_cast<int64_t>(lane) * BS + off) * 8,
+           ar.k[k]);
+    // V: dimension d sits at element (off/4 * D + d) * 4 + off%4 of the tile
+    uint16_t* vt = base + static_cast<int64_t>(a.hkv) * BS * D + static_cast<int64_t>(g) * D * BS;
+    if (2 * lane < D) {
+      const int64_t e = ((off >> 2) * D + 2 * lane) * 4 + (off & 3);
+      vt[e] = static_cast<uint16_t>(ar.v[k]);
+      vt[e + 4] = static_cast<uint16_t>(ar.v[k] >> 16);
+    }
+  }
+}
+
+// pa_decode of a decode step together with its append (one launch: see
+// decode_loop's FUSED, append_load and append_store).
+template <int D, int BS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_bf16_append_kernel(DecodeArgs a, int32_t* __restrict__ queue) {
+  __shared__ DecodeSmem<D> ds;
+  AppendRound<D> ar;
+  append_load<D, BS>(a, ar, 0);
+  const bool cached = decode_scan<D, BS, false>(a, queue, ds);
+  if (cached)
+    decode_loop<D, BS, kCached, false, kMaxGroup, true, true>(a, queue, ds, blockIdx.x, gridDim.x);
+  else
+    decode_loop<D, BS, kNontemporal, false, kMaxGroup, false, true>(a, queue, ds, blockIdx.x,
+                                                                    gridDim.x);
+  append_store<D, BS>(a, ar);
+  // pairs past the first round (batches of more than kAppendRound * 4 * W)
+  const int round = static_cast<int>(gridDim.x) * kWaves * kAppendRound;
+  for (int first = round; first < a.num_seqs * a.hkv; first += round) {
+    append_load<D, BS>(a, ar, first);
+    append_store<D, BS>(a, ar);
+  }
   leave_queue(queue);
 }
 
@@ -2430,7 +2593,10 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int grid, int32_t* queue, hip
     // The persistent kernel merges split-K partitions itself.
     static const int cus = compute_units();
     const int w = min(grid, cus > 0 ? cus : 256);
-    if (a.share != nullptr)
+    if (a.k_new != nullptr)
+      hipLaunchKernelGGL((decode_bf16_append_kernel<D, BS>), dim3(w), dim3(256), 0, st, a,
+                         queue);
+    else if (a.share != nullptr)
       hipLaunchKernelGGL((decode_bf16_shared_kernel<D, BS>), dim3(w), dim3(256), 0, st, a,
                          queue);
     else
@@ -2580,6 +2746,9 @@ DecodeArgs decode_args(void* out, const void* q, const void* pool, const int32_t
   queue = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.queue_off);
   a.n_items = static_cast<int>(static_cast<int64_t>(num_seqs) * ps.num_kv_heads * np_max);
   a.share = nullptr;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
+  a.slots = nullptr;
   return a;
 }
 
@@ -2689,6 +2858,27 @@ hipError_t launch_decode(void* out, const void* q, const void* pool, const int32
                              max_context_len, num_q_heads, ps, scale, workspace, queue);
   a.share = share;  // (only the bf16 persistent decode reads it)
   return dispatch_decode(a, queue, num_q_heads, ps, dtype, st);
+}
+
+hipError_t launch_decode_append(void* out, const void* q, void* pool, const int32_t* tables,
+                                const int32_t* lens, const void* k_new, const void* v_new,
+                                const int32_t* slots, int num_seqs, int max_blocks_per_seq,
+                                int max_context_len, int num_q_heads, const PoolShape& ps,
+                                float scale, int dtype, void* workspace, hipStream_t st) {
+  if (num_seqs == 0) return hipSuccess;
+  if (dtype == 1 && num_seqs <= kMaxScanSeqs) {  // one launch
+    int32_t* queue = nullptr;
+    DecodeArgs a = decode_args(out, q, pool, tables, lens, num_seqs, max_blocks_per_seq,
+                               max_context_len, num_q_heads, ps, scale, workspace, queue);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slots = slots;
+    return dispatch_decode(a, queue, num_q_heads, ps, dtype, st);
+  }
+  // otherwise the append, then the decode, on the same stream
+  if (hipError_t e = launch_append(pool, k_new, v_new, slots, num_seqs, ps, dtype, st)) return e;
+  return launch_decode(out, q, pool, tables, lens, num_seqs, max_blocks_per_seq, max_context_len,
+                       num_q_heads, ps, scale, dtype, workspace, st);
 }
 
 hipError_t launch_decode_noalloc(void* out, const void* q, const void* pool, const int32_t* tables,

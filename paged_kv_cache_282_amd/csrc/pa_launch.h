@@ -76,6 +76,15 @@ hipError_t launch_decode(void* out, const void* q, const void* pool, const int32
                          int dtype, void* workspace, hipStream_t stream,
                          const int32_t* share = nullptr);
 
+// pa_decode_append: the decode step's append and its decode. bfloat16 batches
+// of up to kMaxScanSeqs sequences run in one launch; other calls launch the
+// append, then the decode.
+hipError_t launch_decode_append(void* out, const void* q, void* pool, const int32_t* tables,
+                                const int32_t* lens, const void* k_new, const void* v_new,
+                                const int32_t* slots, int num_seqs, int max_blocks_per_seq,
+                                int max_context_len, int num_q_heads, const PoolShape& ps,
+                                float scale, int dtype, void* workspace, hipStream_t stream);
+
 // pa_decode with the library's own scratch array as the workspace (no
 // allocation). The caller has checked that the packed layout (partials in the
 // call's type) fits kDecodeScratchBytes.

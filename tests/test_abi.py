@@ -37,8 +37,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["pa_append_kv", "pa_copy_blocks", "pa_decode",
                             "pa_decode_workspace_size", "pa_decode_noalloc", "pa_decode_shared",
-                            "pa_prefill_chunk", "pa_mixed_attention", "pa_swap_blocks",
-                            "pa_status_string"])
+                            "pa_decode_append", "pa_prefill_chunk", "pa_mixed_attention",
+                            "pa_swap_blocks", "pa_status_string"])
 
 
 def test_runtime_header_declares_the_runtime():
@@ -133,6 +133,39 @@ def test_decode_shared_validation(lib):
     assert _shared(lib, wsb=16) == WORKSPACE
     assert _shared(lib, q=FAKE) == ALIAS
     assert _shared(lib, out=ctypes.c_void_p(0x10008)) == ALIGN
+
+
+def _decode_append(lib, **kw):
+    a = dict(out=FAKE, q=FAKE2, pool=FAKE, tables=FAKE, lens=FAKE, kn=FAKE, vn=FAKE, slots=FAKE,
+             B=2, MB=4, maxctx=64, hq=8, hkv=2, d=128, bs=16, nb=10, scale=0.1, dtype=BF16,
+             ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.pa_decode_append(a["out"], a["q"], a["pool"], a["tables"], a["lens"], a["kn"],
+                                a["vn"], a["slots"], a["B"], a["MB"], a["maxctx"], a["hq"],
+                                a["hkv"], a["d"], a["bs"], a["nb"], a["scale"], a["dtype"],
+                                a["ws"], a["wsb"], a["stream"])
+
+
+def test_decode_append_validation(lib):
+    """pa_decode_append runs every check of pa_decode, plus those of the new
+    tokens; no call here reaches the device."""
+    assert _decode_append(lib, B=0) == OK
+    assert _decode_append(lib, B=0, kn=None, vn=None, slots=None) == OK
+    assert _decode_append(lib, dtype=7) == UNSUPPORTED
+    assert _decode_append(lib, d=96) == UNSUPPORTED
+    assert _decode_append(lib, hq=7, hkv=2) == SHAPE
+    assert _decode_append(lib, B=-1) == SHAPE
+    assert _decode_append(lib, kn=None) == NULL
+    assert _decode_append(lib, vn=None) == NULL
+    assert _decode_append(lib, slots=None) == NULL
+    assert _decode_append(lib, kn=ctypes.c_void_p(0x10008)) == ALIGN
+    assert _decode_append(lib, vn=ctypes.c_void_p(0x10004)) == ALIGN
+    assert _decode_append(lib, out=None) == NULL
+    assert _decode_append(lib, ws=None) == NULL
+    assert _decode_append(lib, maxctx=65) == SHAPE
+    assert _decode_append(lib, wsb=16) == WORKSPACE
+    assert _decode_append(lib, q=FAKE) == ALIAS
+    assert _decode_append(lib, out=ctypes.c_void_p(0x10008)) == ALIGN
 
 
 def _noalloc(lib, **kw):

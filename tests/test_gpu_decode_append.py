@@ -1,0 +1,99 @@
+"""GPU: pa_decode_append (a decode step's append and its attention in one call).
+
+It must give what pa_append_kv followed by pa_decode gives, bit for bit: the
+outputs, and the whole pool afterwards. Cases cover the one-launch kernel on
+both cache policies (small batches load cached, the full GQA batch streams
+nontemporal), block sizes 16 and 32, head dims 64 and 128, group sizes 1 to
+8, contexts whose new token is the first of a block, of a 32-token step, of
+a partition, and a context of one token; and the fallbacks (over 2048
+sequences, float32), which launch the append and then the decode.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_282_amd as pa
+from tests.gpu_helpers import DeviceStep, bits
+from workloads import build_decode_workload, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _edge_lens(seed, n, hi):
+    """Lengths whose last position starts a block, a step or a partition, a
+    length of one, and random ones."""
+    rng = np.random.default_rng(seed)
+    edge = [1, 2, 16, 17, 32, 33, 1024, 1025, 2048, 2049, 1040, 31]
+    return np.concatenate([edge, rng.integers(1, hi + 1, n - len(edge))])
+
+
+CASES = {
+    "gqa_small_bs16_cached_G8": lambda dt: make_workload(
+        "gqa", dtype=dt, num_seqs=24, median=300, hi=2100, num_q_heads=16, num_kv_heads=2),
+    "gqa_full_bs16_nt_G8": lambda dt: make_workload("gqa", dtype=dt),
+    "mha_G1": lambda dt: make_workload("mha", dtype=dt, num_seqs=12, min_len=1, max_len=3000,
+                                       num_heads=4),
+    "edges_bs32_d64_G4": lambda dt: build_decode_workload(
+        "edges32", 7401, _edge_lens(7400, 40, 3000), 8, 2, 64, 32, dt),
+    "edges_bs16_d128_G2": lambda dt: build_decode_workload(
+        "edges16", 7403, _edge_lens(7402, 40, 3000), 4, 2, 128, 16, dt),
+    "over2048_G2": lambda dt: build_decode_workload(
+        "over2048", 9102, np.random.default_rng(9103).integers(1, 1301, 2100), 4, 2, 64, 16, dt),
+}
+
+
+def _check(w):
+    st = DeviceStep(w)
+    st.copy()
+    pool0 = st.pool.clone()
+    st.append()
+    st.decode()
+    torch.cuda.synchronize()
+    want_out, want_pool = bits(st.out).copy(), st.pool.clone()
+    st.pool.copy_(pool0)
+    out2 = torch.full_like(st.out, float("nan"))
+    pa.pa_decode_append(out2, st.q, st.pool, st.tables, st.lens, st.k_new, st.v_new, st.slots,
+                        w.max_context_len, w.num_kv_heads, w.block_size, w.scale, st.ws)
+    torch.cuda.synchronize()
+    got = bits(out2)
+    bad = np.argwhere((got != want_out).any(axis=2))
+    _say(f"  outputs: {len(bad)} of {got.shape[0] * got.shape[1]} rows differ")
+    assert len(bad) == 0, f"first rows that differ (seq, head): {bad[:5].tolist()}"
+    same_pool = torch.equal(st.pool.view(torch.int16 if st.pool.element_size() == 2 else torch.int32),
+                            want_pool.view(torch.int16 if want_pool.element_size() == 2 else torch.int32))
+    _say(f"  pool bit-identical: {same_pool}")
+    assert same_pool
+    return st, out2
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_append_matches_append_then_decode(name):
+    w = CASES[name]("bf16")
+    assert w.k_new.shape[0] == w.num_seqs, "one new token per sequence"
+    _say(f"[case] decode_append {name}: B={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+         f"d={w.head_dim} bs={w.block_size} max_ctx={w.max_context_len}")
+    _check(w)
+
+
+def test_decode_append_float32_falls_back():
+    w = CASES["edges_bs32_d64_G4"]("f32")
+    _say(f"[case] decode_append f32: B={w.num_seqs}")
+    _check(w)
+
+
+def test_decode_append_repeated_calls():
+    """Back-to-back calls (the queue counters, including the append's, return
+    to zero each time): every call equals the first."""
+    w = CASES["gqa_small_bs16_cached_G8"]("bf16")
+    _say(f"[case] decode_append repeated: B={w.num_seqs}")
+    st, out = _check(w)
+    first = bits(out).copy()
+    for _ in range(3):
+        pa.pa_decode_append(out, st.q, st.pool, st.tables, st.lens, st.k_new, st.v_new, st.slots,
+                            w.max_context_len, w.num_kv_heads, w.block_size, w.scale, st.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), first)
