@@ -24,6 +24,9 @@ Reported (one JSON line on stdout):
              call of about 1.7 GB read + written); `traffic` is the HBM bytes
              per call measured with rocprofv3 counters for this exact kernel
              source (null otherwise)
+  fused_step the same step with each layer's append and decode in one
+             pa_decode_append call (bit-identical outputs and pool), timed per
+             step against the two-call step in the same run, and one such call
   rows       every step of the hot path on its own workload: append, block copy,
              decode on the other batches, chunked prefill -- median time,
              algorithmic bytes or flops, fraction of the matching roofline, and
