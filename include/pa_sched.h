@@ -183,7 +183,9 @@ int pa_sched_step(pa_sched* s, int32_t* buf, int64_t cap, int64_t* used);
  * Every iteration's packet goes host -> device with one asynchronous copy
  * from a pinned ring slot, then pa_copy_blocks and pa_append_kv are
  * enqueued, then the attention: pa_mixed_attention when the iteration has
- * both prefill chunks and decodes, else pa_prefill_chunk or pa_decode. There are no model weights:
+ * both prefill chunks and decodes, else pa_prefill_chunk or pa_decode (an
+ * iteration of decodes only runs its append and decode as one
+ * pa_decode_append). There are no model weights:
  * queries and new K/V rows come from caller buffers, row i of the
  * iteration's tokens (prefill tokens first, then decode tokens) reading row i
  * of k_rows / v_rows, prefill token i reading row i of q_prefill and decode i

@@ -630,6 +630,12 @@ struct pa_engine {
                                   dtype, stream))
         return st;
     }
+    // A decode-only iteration appends one token per decoding sequence, rows in
+    // decode order: its append and attention go in one launch.
+    if (n_chunks == 0 && n_pre == 0 && n_dec > 0 && n_slots == n_dec)
+      return pa_decode_append(out_decode, q_decode, pool, dec_tab, dec_ctx, k_rows, v_rows, slots,
+                              n_dec, mb, c.max_len, hq, hkv, d, c.block_size, c.num_blocks, scale,
+                              dtype, ws, ws_bytes, stream);
     if (int st = pa_append_kv(pool, k_rows, v_rows, slots, n_slots, c.num_blocks, hkv, d,
                               c.block_size, dtype, stream))
       return st;
