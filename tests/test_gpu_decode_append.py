@@ -5,7 +5,8 @@ outputs, and the whole pool afterwards. Cases cover the one-launch kernel on
 both cache policies (small batches load cached, the full GQA batch streams
 nontemporal), block sizes 16 and 32, head dims 64 and 128, group sizes 1 to
 8, contexts whose new token is the first of a block, of a 32-token step, of
-a partition, and a context of one token; and the fallbacks (over 2048
+a partition, and a context of one token, and a batch with more new tokens
+than the kernel's first append round holds; and the fallbacks (over 2048
 sequences, float32), which launch the append and then the decode.
 """
 import numpy as np
@@ -41,6 +42,10 @@ CASES = {
         "edges32", 7401, _edge_lens(7400, 40, 3000), 8, 2, 64, 32, dt),
     "edges_bs16_d128_G2": lambda dt: build_decode_workload(
         "edges16", 7403, _edge_lens(7402, 40, 3000), 4, 2, 128, 16, dt),
+    # 8000 (sequence, kv head) pairs: more than one round of the kernel's
+    # append (2 pairs per wave), so the pairs past it are written after the loop
+    "many_pairs_G1": lambda dt: build_decode_workload(
+        "many", 7405, np.random.default_rng(7404).integers(1, 200, 1000), 8, 8, 64, 16, dt),
     "over2048_G2": lambda dt: build_decode_workload(
         "over2048", 9102, np.random.default_rng(9103).integers(1, 1301, 2100), 4, 2, 64, 16, dt),
 }
